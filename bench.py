@@ -1,0 +1,204 @@
+"""Benchmark of the forward step on one MI355X.
+
+Workload: the full 33B shape (52 blocks, hidden 7168, 56/8 heads of 128, FFN
+22016, vocabulary 166,912, 61.69 GiB of bf16 weights, seeded random init),
+batch 1: a 2,048-token uniform-random prompt prefilled as one chunk, then 128
+greedy decode steps whose tokens stay on the GPU.  One benchmark step is that
+whole request.  Reported value: decode tokens per second over the timed steps
+(HIP events on the stream the library runs on); beside it prefill tokens per
+second, the decode HBM rate against the 8 TB/s peak, the dominant kernel's
+roofline fraction, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def ensure_built():
+    need = [os.path.join(ROOT, "dense_gqa_llama_amd", "libllama_mi355x.so"),
+            os.path.join(ROOT, "synth", "libsynth_dev.so"), os.path.join(ROOT, "synth", "libsynth.so"),
+            os.path.join(ROOT, "oracle", "liboracle.so")]
+    if not all(os.path.exists(p) for p in need):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+def gate_up_bytes(g, rows=1):
+    """Algorithmic bytes of one decode gate/up launch: both weight matrices
+    once, the normed input rows, the SwiGLU output rows."""
+    return 2 * g.ffn * g.hidden * 2 + rows * g.hidden * 2 + rows * g.ffn * 2
+
+
+def decode_bytes(g, T):
+    """Algorithmic bytes of one decode token at context T (positions 0..T-1
+    before the new row): every weight once (one embedding row), the cache's
+    keys and values read for T+1 positions, the new row's keys and values
+    written."""
+    kvp = g.kv_bytes_per_position()
+    return g.decode_weight_bytes() + (T + 1) * kvp + kvp
+
+
+def cpu_baseline(g, T, reps=3):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    one decode row through one 33B block at context T (cache drawn N(0,1)) and
+    one lm_head row; a token costs 52 block rows plus the head row."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth.workloads import TensorIds
+    from tests.host_inputs import HostWeights
+
+    W = HostWeights(g)
+    blk = {k: W(f"b0.{k}") for k in ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up",
+                                      "down")}
+    kc = synth.normal_bf16((T + 1) * g.kv_dim, 9001, TensorIds.K_CACHE).reshape(
+        T + 1, g.n_kv_heads, g.head_dim)
+    vc = synth.normal_bf16((T + 1) * g.kv_dim, 9001, TensorIds.V_CACHE).reshape(
+        T + 1, g.n_kv_heads, g.head_dim)
+    row = synth.normal_bf16(g.hidden, 9002, TensorIds.INPUT_ROWS).reshape(1, g.hidden)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.block(g, blk, kc, vc, np.array([T], dtype=np.int32), row)
+    t_block = (time.perf_counter() - t0) / reps
+    lm = W("lm_head")
+    t0 = time.perf_counter()
+    oracle.linear(row, lm)
+    t_head = time.perf_counter() - t0
+    t_tok = g.n_exec * t_block + t_head
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": 1.0 / t_tok, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{reps} decode rows through one 33B block at context {T} "
+                       f"({t_block:.3f} s each) + one lm_head row ({t_head:.3f} s); "
+                       f"a token = {g.n_exec} block rows + 1 head row")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    ensure_built()
+    import torch
+
+    import dense_gqa_llama_amd as L
+    from dense_gqa_llama_amd import binding as B
+    from synth import device as sd
+    from synth.workloads import config
+
+    g = config(3)
+    P, D = g.prompt_len, g.decode_steps
+    cap = P + D
+    torch.cuda.set_device(0)
+    log(f"generating {g.params() * 2 / 2**30:.2f} GiB of weights on the GPU")
+    w = sd.weights(g)
+    torch.cuda.synchronize()
+    model = L.Model(g, w, max_positions=cap, max_chunk_rows=P, max_window_rows=16, max_seqs=2)
+    seq = model.new_sequence(cap)
+    prompt = sd.tokens(P, g.prompt_seeds[0], 0, g.vocab)
+    stream = torch.cuda.current_stream()
+
+    def request():
+        """One request: prefill + D greedy steps; returns (prefill ms, decode ms)."""
+        seq.set_length(0)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        out = model.prefill(seq, tokens=prompt, want_logits=False)
+        e1.record(stream)
+        nxt = out["next"]
+        buf = torch.empty(D, dtype=torch.int32, device="cuda")
+        buf[0:1].copy_(nxt)
+        for i in range(1, D):
+            model.decode([seq], tokens=buf[i - 1:i], want_logits=False, next_out=buf[i:i + 1])
+        e2.record(stream)
+        return e0, e1, e2, buf
+
+    for i in range(args.warmup):
+        log(f"warmup step {i}")
+        request()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    evs = [request() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    model.check_finite()
+    pre_ms = sum(a.elapsed_time(b) for a, b, _, _ in evs)
+    dec_ms = sum(b.elapsed_time(c) for _, b, c, _ in evs)
+    # the first generated token comes from the prefill; D - 1 decode steps follow
+    dec_tokens = args.steps * (D - 1)
+    dec_tps = dec_tokens / (dec_ms / 1e3)
+    pre_tps = args.steps * P / (pre_ms / 1e3)
+    avg_T = P + (D - 1) / 2.0
+    dec_gbs = decode_bytes(g, avg_T) * dec_tokens / (dec_ms / 1e3) / 1e9
+    toks = evs[-1][3].cpu().tolist()
+    log(f"decode {dec_tps:.2f} tok/s ({dec_gbs:.0f} GB/s), prefill {pre_tps:.0f} tok/s, "
+        f"first tokens {toks[:8]}")
+
+    # dominant kernel: the decode gate/up projection (53% of a token's bytes)
+    B.llama_set_timing(model.handle, "gate_up", g.n_exec * D)
+    request()
+    torch.cuda.synchronize()
+    ms, n = B.llama_timing_read(model.handle)
+    B.llama_set_timing(model.handle, "off")
+    per_launch_ms = ms / max(n, 1)
+    achieved = gate_up_bytes(g) / (per_launch_ms / 1e3) / 1e9
+    log(f"gate/up projection: {n} launches, {per_launch_ms * 1e3:.1f} us each, "
+        f"{achieved:.0f} GB/s")
+
+    result = {
+        "metric": "decode tok/s + HBM GB/s (% peak), 33B bf16 batch 1; prefill tok/s",
+        "value": round(dec_tps, 3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded random-init weights ~N(0,0.02) (norms 1+N(0,0.02)), "
+                "uniform random prompt tokens",
+        "config": {"workload": "33B-shaped dense GQA Llama (52 blocks, hidden 7168, 56/8 heads "
+                               "of 128, FFN 22016, vocab 166912), 2048-token prompt in one "
+                               "chunk + 128 greedy decode steps, batch 1",
+                   "prompt_tokens": P, "decode_steps": D, "batch": 1, "parallelism": "none"},
+        "decode_ms_per_token": round(dec_ms / dec_tokens, 4),
+        "decode_hbm_gbs": round(dec_gbs, 1),
+        "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "prefill_tok_s": round(pre_tps, 1),
+        "roofline": {"bound": "hbm", "kernel": "decode gate/up projection + SwiGLU (R=1)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_us": round(per_launch_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        result["cpu_baseline"] = cpu_baseline(g, int(avg_T))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+// Decode row projections: y[r][n] = sum_k W[n][k] x[r][k] for windows of
+// 1..16 rows, fp32 sums rounded once to bf16 (pull request "llama:
+// Nanbeige4.3-33B on Metal, the bf16 release served as published", section
+// "How": decode windows with fp32 sums rounded once).
+//
+// HBM-bound: every weight byte is read once per step.  Each wave owns a few
+// output rows n; lane l reads W[n][8l + 512j .. +8] as one 16-byte load (a
+// wave reads 1 KiB of a row per step, fully coalesced) and accumulates with
+// v_dot2c_f32_bf16 into per-(n, r) fp32 partials, then a fixed xor butterfly
+// sums the 64 lanes.  The order of every partial sum depends only on K, never
+// on the window size R or on the batch, so a row computed inside a 16-row
+// window equals the same row computed alone, bit for bit.
+#include "common.h"
+#include "launch.h"
+
+struct GemvArgs {
+  GemvSeg seg[3];
+  int nseg;
+  int K;
+  const bf16_t* x;
+  int ldx;
+  bf16_t* out;
+  int ldo;
+  float* out32;
+  int ld32;
+};
+
+__device__ __forceinline__ float silu_bf16(float g) { return rbf(g / (1.0f + expf(-g))); }
+
+// NR weight rows per wave; for SWIGLU the first NR/2 come from the gate
+// matrix and the last NR/2 from the up matrix, for the same output columns.
+template <int R, int NR, int EPI>
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+  constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * 4 + wave) * COLS;  // first output column of this wave
+
+  const u32x4_t* wp[NR];
+  int nloc = n0;
+  if (EPI == GEMV_SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const bf16_t* W = i < COLS ? a.seg[0].W : a.seg[1].W;
+      wp[i] = (const u32x4_t*)(W + (size_t)(n0 + (i % COLS)) * a.K);
+    }
+  } else {
+    const bf16_t* W = a.seg[0].W;
+    int base = a.seg[0].n_begin;
+    for (int s = 1; s < a.nseg; ++s)
+      if (n0 >= a.seg[s].n_begin) { W = a.seg[s].W; base = a.seg[s].n_begin; }
+    nloc = n0 - base;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) wp[i] = (const u32x4_t*)(W + (size_t)(nloc + i) * a.K);
+  }
+
+  float acc[NR][R];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[i][r] = 0.f;
+
+  const int nv = a.K >> 3;
+  const u32x4_t* xb = (const u32x4_t*)a.x;
+  const int xs = a.ldx >> 3;
+#pragma unroll 2
+  for (int v = lane; v < nv; v += WAVE) {
+    u32x4_t w[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) w[i] = __builtin_nontemporal_load(wp[i] + v);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      u32x4_t xv = xb[r * xs + v];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        float t = acc[i][r];
+        t = dot2(w[i].x, xv.x, t);
+        t = dot2(w[i].y, xv.y, t);
+        t = dot2(w[i].z, xv.z, t);
+        t = dot2(w[i].w, xv.w, t);
+        acc[i][r] = t;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[i][r] = wave_sum(acc[i][r]);
+
+  // Spread the stores over lanes: lane (c*R + r) writes column c of row r.
+#pragma unroll
+  for (int c = 0; c < COLS; ++c) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (lane != (c * R + r) % WAVE) continue;
+      const int n = n0 + c;
+      if (EPI == GEMV_STORE) {
+        a.out[(size_t)r * a.ldo + n] = f2bf(acc[c][r]);
+        if (a.out32) a.out32[(size_t)r * a.ld32 + n] = acc[c][r];
+      } else if (EPI == GEMV_RESIDUAL) {
+        bf16_t* h = a.out + (size_t)r * a.ldo + n;
+        *h = f2bf(bf2f(*h) + rbf(acc[c][r]));
+      } else {
+        float g = rbf(acc[c][r]), u = rbf(acc[c + COLS][r]);
+        a.out[(size_t)r * a.ldo + n] = f2bf(silu_bf16(g) * u);
+      }
+    }
+  }
+}
+
+template <int R, int EPI>
+static void launch_r(const GemvArgs& a, int N, hipStream_t s) {
+  // weight rows per wave: more for small windows (more bytes in flight per
+  // wave), fewer for large ones (register budget of the R*NR partials).
+  constexpr int NR = EPI == GEMV_SWIGLU ? (R <= 4 ? 4 : 2) : (R <= 2 ? 4 : 2);
+  constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
+  int grid = N / (4 * COLS);
+  hipLaunchKernelGGL((gemv_kernel<R, NR, EPI>), dim3(grid), dim3(256), 0, s, a);
+}
+
+template <int EPI>
+static void launch_epi(int rows, const GemvArgs& a, int N, hipStream_t s) {
+  switch (rows) {
+#define CASE(R) \
+  case R: launch_r<R, EPI>(a, N, s); break;
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+    CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
+#undef CASE
+    default: break;
+  }
+}
+
+// Column counts must be multiples of 16 (every served width is a multiple of
+// 128), so no wave straddles a segment or the end.
+void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* x, int ldx,
+                 int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s) {
+  GemvArgs a;
+  for (int i = 0; i < 3; ++i) a.seg[i] = i < nseg ? seg[i] : seg[0];
+  a.nseg = nseg;
+  a.K = K;
+  a.x = (const bf16_t*)x;
+  a.ldx = ldx;
+  a.out = (bf16_t*)out;
+  a.ldo = ldo;
+  a.out32 = out32;
+  a.ld32 = ld32;
+  if (epi == GEMV_STORE) launch_epi<GEMV_STORE>(rows, a, N, s);
+  else if (epi == GEMV_RESIDUAL) launch_epi<GEMV_RESIDUAL>(rows, a, N, s);
+  else launch_epi<GEMV_SWIGLU>(rows, a, N, s);
+}

@@ -1,0 +1,244 @@
+// Glue kernels of the forward step: embedding gather, RMSNorm, RoPE with the
+// cache write, greedy argmax.  Rounding points follow the pull request
+// "llama: Nanbeige4.3-33B on Metal, the bf16 release served as published",
+// section "How".
+#include "common.h"
+#include "launch.h"
+
+__global__ void fill_zero_kernel(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+void launch_fill_zero(int* p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(64), 0, s, p, n);
+}
+
+// ------------------------------------------------------------ embedding ----
+// h[r] = E[tok[r]] (a copy); an id outside [0, vocab) yields a NaN row, which
+// the greedy draw then refuses, rather than an out-of-bounds read.
+__global__ __launch_bounds__(256) void embed_kernel(const bf16_t* __restrict__ E, int vocab,
+                                                    int H, const int32_t* __restrict__ tok,
+                                                    bf16_t* __restrict__ h) {
+  int r = blockIdx.x;
+  int t = tok[r];
+  uint4* dst = (uint4*)(h + (size_t)r * H);
+  int nv = H / 8;
+  if (t < 0 || t >= vocab) {
+    uint4 nan = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    for (int i = threadIdx.x; i < nv; i += blockDim.x) dst[i] = nan;
+    return;
+  }
+  const uint4* src = (const uint4*)(E + (size_t)t * H);
+  for (int i = threadIdx.x; i < nv; i += blockDim.x) dst[i] = src[i];
+}
+
+void launch_embed(const void* E, int vocab, int H, const int32_t* tok, void* h, int rows,
+                  hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, s, (const bf16_t*)E, vocab, H, tok,
+                     (bf16_t*)h);
+}
+
+// -------------------------------------------------------------- RMSNorm ----
+// out = bf16(w * bf16(x * r)), r = 1/sqrt(sum(x^2)/H + eps).  One 256-thread
+// workgroup per row; each thread sums its 8-element slices in order, then the
+// four waves' sums are added in wave order, so every row (whatever the batch)
+// sees the same association.  In place (out == h) is allowed: after the
+// barrier that completes the sum, each element is read and then written by
+// one thread only.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const bf16_t* h, const bf16_t* __restrict__ w,
+                                                      bf16_t* out, int H, float eps) {
+  __shared__ float part[4];
+  int r = blockIdx.x;
+  const uint4* x = (const uint4*)(h + (size_t)r * H);
+  int nv = H / 8;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < nv; i += 256) {
+    uint4 v = x[i];
+    uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = bf_lo(q[j]), b = bf_hi(q[j]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane_id() == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  float rs = 1.0f / sqrtf(tot / (float)H + eps);
+  const uint4* wv = (const uint4*)w;
+  uint4* o = (uint4*)(out + (size_t)r * H);
+  for (int i = threadIdx.x; i < nv; i += 256) {
+    uint4 v = x[i], g = wv[i];
+    uint32_t q[4] = {v.x, v.y, v.z, v.w}, ww[4] = {g.x, g.y, g.z, g.w}, res[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float n0 = rbf(bf_lo(q[j]) * rs), n1 = rbf(bf_hi(q[j]) * rs);
+      res[j] = pack_bf2(f2bf(bf_lo(ww[j]) * n0), f2bf(bf_hi(ww[j]) * n1));
+    }
+    o[i] = make_uint4(res[0], res[1], res[2], res[3]);
+  }
+}
+
+void launch_rmsnorm(const void* h, const void* w, void* out, int rows, int H, float eps,
+                    hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, (const bf16_t*)h,
+                     (const bf16_t*)w, (bf16_t*)out, H, eps);
+}
+
+// ------------------------------------------------------- RoPE + caching ----
+// Unscaled NeoX RoPE on the q and k heads of each row, then k and v stored at
+// slot p of the row's cache (Nanbeige4.3-33B NInfer card, "Provenance and
+// representation": half-head pairs (i, i + d/2), theta 1.2e8).
+//   inv_i = fp32(1 / fp32(theta^(2i/d))), angle a = fp32(p * inv_i),
+//   c, s = bf16(fp32(cos a)), bf16(fp32(sin a)),
+//   x'_i = bf16(bf16(x_i c) + bf16(-x_{i+d/2} s)),
+//   x'_{i+d/2} = bf16(bf16(x_{i+d/2} c) + bf16(x_i s)).
+// cos, sin and the power are evaluated in binary64 and rounded to fp32.
+// One workgroup per row; qkv is the projection output [rows][qd + 2*kvd].
+__global__ __launch_bounds__(256) void rope_kv_kernel(const bf16_t* __restrict__ qkv,
+                                                      bf16_t* __restrict__ qout, RowTable tab,
+                                                      int nq, int nkv, int d, float theta) {
+  __shared__ float inv[64];
+  __shared__ float cs[64], sn[64];
+  int rt = blockIdx.x;
+  int seq = rt / tab.rows_per_seq;
+  int p = tab.pos0[seq] + rt % tab.rows_per_seq;
+  int half = d / 2;
+  if (threadIdx.x < half) {
+    int i = threadIdx.x;
+    float e = (float)(2 * i) / (float)d;
+    float pw = (float)pow((double)theta, (double)e);
+    inv[i] = 1.0f / pw;
+    float a = __fmul_rn((float)p, inv[i]);
+    cs[i] = rbf((float)cos((double)a));
+    sn[i] = rbf((float)sin((double)a));
+  }
+  __syncthreads();
+  int qd = nq * d, kvd = nkv * d;
+  const bf16_t* src = qkv + (size_t)rt * (qd + 2 * kvd);
+  bf16_t* kdst = tab.k[seq] + (size_t)p * kvd;
+  bf16_t* vdst = tab.v[seq] + (size_t)p * kvd;
+  int items = (nq + nkv) * half;
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    int hh = it / half, i = it % half;
+    const bf16_t* x = src + hh * d;  // q heads then k heads, contiguous
+    float x1 = bf2f(x[i]), x2 = bf2f(x[i + half]);
+    float c = cs[i], s = sn[i];
+    bf16_t o1 = f2bf(rbf(x1 * c) + rbf(-x2 * s));
+    bf16_t o2 = f2bf(rbf(x2 * c) + rbf(x1 * s));
+    bf16_t* dst = hh < nq ? qout + (size_t)rt * qd + hh * d : kdst + (hh - nq) * d;
+    dst[i] = o1;
+    dst[i + half] = o2;
+  }
+  const uint32_t* vs = (const uint32_t*)(src + qd + kvd);
+  uint32_t* vd = (uint32_t*)vdst;
+  for (int i = threadIdx.x; i < kvd / 2; i += blockDim.x) vd[i] = vs[i];
+}
+
+void launch_rope_kv(const void* qkv, void* qout, const RowTable& tab, int rows, int nq, int nkv,
+                    int d, float theta, hipStream_t s) {
+  hipLaunchKernelGGL(rope_kv_kernel, dim3(rows), dim3(256), 0, s, (const bf16_t*)qkv,
+                     (bf16_t*)qout, tab, nq, nkv, d, theta);
+}
+
+// --------------------------------------------------------------- SwiGLU ----
+// m = bf16(bf16(silu(g)) * u) over gu = [rows][2F] (gate then up halves).
+__global__ __launch_bounds__(256) void swiglu_kernel(const bf16_t* __restrict__ gu,
+                                                     bf16_t* __restrict__ m, int F, int rows) {
+  size_t n = (size_t)rows * F;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x) {
+    size_t r = i / F, j = i % F;
+    float g = bf2f(gu[r * 2 * F + j]), u = bf2f(gu[r * 2 * F + F + j]);
+    float sg = rbf(g / (1.0f + expf(-g)));
+    m[i] = f2bf(sg * u);
+  }
+}
+
+void launch_swiglu(const void* gu, void* m, int F, int rows, hipStream_t s) {
+  size_t n = (size_t)rows * F;
+  int grid = (int)((n + 255) / 256);
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(swiglu_kernel, dim3(grid), dim3(256), 0, s, (const bf16_t*)gu, (bf16_t*)m,
+                     F, rows);
+}
+
+// --------------------------------------------------------------- argmax ----
+// Greedy draw over bf16 logits: largest value, ties to the lowest id (review
+// reply "Teacher-forced misses"); a row holding NaN or +-Inf yields -1 and
+// raises the model's non-finite flag.  Stage 1: each workgroup scans one
+// chunk of a row.  Stage 2: one wave merges a row's chunks in order.
+#define ARGMAX_CHUNK 4096
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void argmax_partial_kernel(const bf16_t* __restrict__ logits,
+                                                             int V, int ld, float* pv, int* pi,
+                                                             int nchunk) {
+  __shared__ float sv[4];
+  __shared__ int si[4], sbad[4];
+  int c = blockIdx.x, r = blockIdx.y;
+  const bf16_t* row = logits + (size_t)r * ld;
+  int beg = c * ARGMAX_CHUNK, end = min(V, beg + ARGMAX_CHUNK);
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF, bad = 0;
+  for (int i = beg + threadIdx.x; i < end; i += 256) {
+    float v = bf2f(row[i]);
+    if (!isfinite(v)) bad = 1;
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    float ov = __shfl_xor(bv, m, WAVE);
+    int oi = __shfl_xor(bi, m, WAVE);
+    bad |= __shfl_xor(bad, m, WAVE);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  int w = threadIdx.x >> 6;
+  if (lane_id() == 0) { sv[w] = bv; si[w] = bi; sbad[w] = bad; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bv = sv[0]; bi = si[0]; bad = sbad[0];
+    for (int k = 1; k < 4; ++k) {
+      if (better(sv[k], si[k], bv, bi)) { bv = sv[k]; bi = si[k]; }
+      bad |= sbad[k];
+    }
+    pv[r * nchunk + c] = bad ? NAN : bv;
+    pi[r * nchunk + c] = bi;
+  }
+}
+
+__global__ __launch_bounds__(64) void argmax_final_kernel(const float* pv, const int* pi,
+                                                          int nchunk, int32_t* out, int* flag) {
+  int r = blockIdx.x;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF, bad = 0;
+  for (int c = lane_id(); c < nchunk; c += WAVE) {
+    float v = pv[r * nchunk + c];
+    if (isnan(v)) bad = 1;
+    else if (better(v, pi[r * nchunk + c], bv, bi)) { bv = v; bi = pi[r * nchunk + c]; }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    float ov = __shfl_xor(bv, m, WAVE);
+    int oi = __shfl_xor(bi, m, WAVE);
+    bad |= __shfl_xor(bad, m, WAVE);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  if (lane_id() == 0) {
+    if (out) out[r] = bad ? -1 : bi;
+    if (bad) atomicOr(flag, 1);
+  }
+}
+
+int argmax_chunks(int V) { return (V + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK; }
+
+void launch_argmax(const void* logits, int V, int ld, int rows, float* pv, int* pi,
+                   int32_t* out, int* flag, hipStream_t s) {
+  int nchunk = argmax_chunks(V);
+  hipLaunchKernelGGL(argmax_partial_kernel, dim3(nchunk, rows), dim3(256), 0, s,
+                     (const bf16_t*)logits, V, ld, pv, pi, nchunk);
+  hipLaunchKernelGGL(argmax_final_kernel, dim3(rows), dim3(64), 0, s, pv, pi, nchunk, out, flag);
+}

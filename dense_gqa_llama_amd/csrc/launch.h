@@ -1,0 +1,49 @@
+// Host-side launchers of the gfx950 kernels (defined in the k_*.hip files and
+// called by the C-ABI layer in llama_abi.cpp).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define LLAMA_MAX_SEQS 16
+
+// Where each row of a step lives: row rt belongs to sequence rt / rows_per_seq
+// at position pos0[seq] + rt % rows_per_seq; k / v are that sequence's key and
+// value slabs for the execution being run ([max_positions][n_kv_heads][d]).
+struct RowTable {
+  uint16_t* k[LLAMA_MAX_SEQS];
+  uint16_t* v[LLAMA_MAX_SEQS];
+  int pos0[LLAMA_MAX_SEQS];
+  int rows_per_seq;
+};
+
+void launch_fill_zero(int* p, int n, hipStream_t s);
+void launch_embed(const void* E, int vocab, int H, const int32_t* tok, void* h, int rows,
+                  hipStream_t s);
+void launch_rmsnorm(const void* h, const void* w, void* out, int rows, int H, float eps,
+                    hipStream_t s);
+void launch_rope_kv(const void* qkv, void* qout, const RowTable& tab, int rows, int nq, int nkv,
+                    int d, float theta, hipStream_t s);
+void launch_swiglu(const void* gu, void* m, int F, int rows, hipStream_t s);
+int argmax_chunks(int V);
+void launch_argmax(const void* logits, int V, int ld, int rows, float* pv, int* pi, int32_t* out,
+                   int* flag, hipStream_t s);
+
+// Decode projections (1..16 rows).  Output columns [0, N) are the
+// concatenation of up to three weight matrices (segments), each [rows][K].
+enum GemvEpilogue { GEMV_STORE = 0, GEMV_RESIDUAL = 1, GEMV_SWIGLU = 2 };
+struct GemvSeg {
+  const uint16_t* W;
+  int n_begin, n_end;
+};
+// STORE:    out[r*ldo + n] = bf16(acc); out32 (nullable) gets the fp32 sum.
+// RESIDUAL: out[r*ldo + n] = bf16(out + bf16(acc))  (the residual stream).
+// SWIGLU:   seg[0] = gate, seg[1] = up, both with n in [0, F):
+//           out[r*ldo + n] = bf16(bf16(silu(bf16(g))) * bf16(u)).
+void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* x, int ldx,
+                 int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s);
+
+// Decode attention: split over key blocks at absolute positions, then a
+// merge in block order.
+int attn_key_block();
+void launch_attn_decode(const void* q, const RowTable& tab, int rows, int nq, int nkv, int d,
+                        float* part, int max_blocks, void* out, hipStream_t s);

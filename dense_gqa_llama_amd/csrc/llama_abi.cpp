@@ -1,0 +1,590 @@
+// C-ABI layer: argument validation, handles, workspace layout and the order in
+// which a step's kernels are enqueued.  Declarations and contracts are in
+// include/llama_mi355x.h.
+#include "llama_mi355x.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Device workspace carved into fixed regions.
+struct Layout {
+  size_t h, x, qkv, q, att, gu, m, logits, amx_v, amx_i, part, flag, total;
+};
+
+struct Dims {
+  int H, nq, nkv, d, qd, kvd, F, V, nexec;
+  int M;      // largest number of rows one pass carries
+  int Mdec;   // rows of one decode step (seqs * window)
+  int Llog;   // rows of the internal logits buffer
+  int max_blocks;
+};
+
+Dims dims_of(const llama_config& c, int max_positions) {
+  Dims d{};
+  d.H = c.hidden;
+  d.nq = c.n_q_heads;
+  d.nkv = c.n_kv_heads;
+  d.d = c.head_dim;
+  d.qd = c.n_q_heads * c.head_dim;
+  d.kvd = c.n_kv_heads * c.head_dim;
+  d.F = c.ffn;
+  d.V = c.vocab;
+  d.nexec = c.n_blocks * c.n_loops;
+  d.Mdec = c.max_seqs * c.max_window_rows;
+  // prompt chunks currently run as windows of up to 16 rows
+  d.M = std::max(d.Mdec, std::min(16, c.max_chunk_rows));
+  d.Llog = std::max(d.Mdec, 16);
+  d.max_blocks = (max_positions + attn_key_block() - 1) / attn_key_block();
+  return d;
+}
+
+Layout layout_of(const Dims& d) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  L.h = take((size_t)d.M * d.H * 2);
+  L.x = take((size_t)d.M * std::max(d.H, d.qd) * 2);
+  L.qkv = take((size_t)d.M * (d.qd + 2 * d.kvd) * 2);
+  L.q = take((size_t)d.M * d.qd * 2);
+  L.att = take((size_t)d.M * d.qd * 2);
+  L.gu = take((size_t)d.M * 2 * d.F * 2);
+  L.m = take((size_t)d.M * d.F * 2);
+  int nch = d.V ? argmax_chunks(d.V) : 1;
+  L.logits = take((size_t)d.Llog * std::max(d.V, 1) * 2);
+  L.amx_v = take((size_t)d.Llog * nch * 4);
+  L.amx_i = take((size_t)d.Llog * nch * 4);
+  L.part = take((size_t)d.M * d.nq * d.max_blocks * (d.d + 2) * 4);
+  L.flag = take(256);
+  L.total = off;
+  return L;
+}
+
+int check_config(const llama_config* c) {
+  if (!c) return fail(LLAMA_E_ARG, "config is NULL");
+  if (c->n_blocks < 1 || c->n_loops < 1)
+    return fail(LLAMA_E_GEOMETRY, "n_blocks and n_loops must be at least 1");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(LLAMA_E_GEOMETRY, "head_dim %d is not served (64 or 128)", c->head_dim);
+  if (c->hidden <= 0 || c->hidden % 128)
+    return fail(LLAMA_E_GEOMETRY, "hidden %d is not a positive multiple of 128", c->hidden);
+  if (c->ffn <= 0 || c->ffn % 128)
+    return fail(LLAMA_E_GEOMETRY, "ffn %d is not a positive multiple of 128", c->ffn);
+  if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads)
+    return fail(LLAMA_E_GEOMETRY, "%d query heads do not split over %d KV heads", c->n_q_heads,
+                c->n_kv_heads);
+  if (c->n_q_heads / c->n_kv_heads > 8)
+    return fail(LLAMA_E_GEOMETRY, "more than 8 query heads per KV head");
+  if ((c->n_q_heads * c->head_dim) % 128 || (c->n_kv_heads * c->head_dim) % 128)
+    return fail(LLAMA_E_GEOMETRY, "head widths must total multiples of 128");
+  if (c->vocab < 0 || c->vocab % 128)
+    return fail(LLAMA_E_GEOMETRY, "vocab %d is not a multiple of 128", c->vocab);
+  if (!(c->rope_theta > 0.0)) return fail(LLAMA_E_GEOMETRY, "rope_theta must be positive");
+  if (!(c->rms_eps >= 0.0f)) return fail(LLAMA_E_GEOMETRY, "rms_eps must be non-negative");
+  if (c->max_chunk_rows < 1 || c->max_chunk_rows > 2048)
+    return fail(LLAMA_E_GEOMETRY, "max_chunk_rows must be 1..2048");
+  if (c->max_window_rows < 1 || c->max_window_rows > 16)
+    return fail(LLAMA_E_GEOMETRY, "max_window_rows must be 1..16");
+  if (c->max_seqs < 1 || c->max_seqs > LLAMA_MAX_SEQS)
+    return fail(LLAMA_E_GEOMETRY, "max_seqs must be 1..%d", LLAMA_MAX_SEQS);
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+struct llama_model {
+  llama_config cfg;
+  Dims d;
+  Layout L;
+  std::vector<llama_block_weights> blocks;
+  const void* embed;
+  const void* final_norm;
+  const void* lm_head;
+  uint8_t* ws;
+  int max_positions;
+  void* cap;
+  size_t cap_bytes;
+  bool flag_ready;  // the non-finite flag has been cleared on the device
+  // measurement hook
+  int timing_kernel = 0;
+  std::vector<hipEvent_t> tev;  // pairs
+  size_t tused = 0;
+  template <typename T>
+  T* at(size_t off) const {
+    return (T*)(ws + off);
+  }
+};
+
+struct llama_kv {
+  llama_model* model;
+  uint8_t* buf;
+  int max_positions;
+  int length;
+  size_t slab;  // bytes of one execution's keys (or values)
+};
+
+namespace {
+
+int dev_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(LLAMA_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return LLAMA_OK;
+}
+
+// Rows [row0, row0 + rows) of the pass over sequences kvs[0..nseq) with
+// `rows_per_seq` rows each, starting at positions pos0[s].
+struct Pass {
+  llama_model* m;
+  llama_kv* const* kvs;
+  int nseq;
+  int rows_per_seq;
+  int pos0[LLAMA_MAX_SEQS];
+  hipStream_t s;
+};
+
+RowTable table_for(const Pass& p, int exec) {
+  RowTable t{};
+  for (int i = 0; i < p.nseq; ++i) {
+    uint8_t* base = p.kvs[i]->buf + (size_t)exec * 2 * p.kvs[i]->slab;
+    t.k[i] = (uint16_t*)base;
+    t.v[i] = (uint16_t*)(base + p.kvs[i]->slab);
+    t.pos0[i] = p.pos0[i];
+  }
+  t.rows_per_seq = p.rows_per_seq;
+  return t;
+}
+
+// Event pair around launches of the measured kernel class.
+struct Timed {
+  llama_model* m;
+  hipStream_t s;
+  bool on;
+  Timed(llama_model* m_, int cls, hipStream_t s_) : m(m_), s(s_) {
+    on = m->timing_kernel == cls && m->tused + 2 <= m->tev.size();
+    if (on) (void)hipEventRecord(m->tev[m->tused], s);
+  }
+  ~Timed() {
+    if (on) {
+      (void)hipEventRecord(m->tev[m->tused + 1], s);
+      m->tused += 2;
+    }
+  }
+};
+
+// Projection over all rows in launches of at most 16 rows.
+void gemv_rows(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* x, int ldx,
+               int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s) {
+  for (int r0 = 0; r0 < rows; r0 += 16) {
+    int n = std::min(16, rows - r0);
+    launch_gemv(epi, seg, nseg, N, K, (const uint16_t*)x + (size_t)r0 * ldx, ldx, n,
+                (uint16_t*)out + (size_t)r0 * ldo, ldo, out32 ? out32 + (size_t)r0 * ld32 : nullptr,
+                ld32, s);
+  }
+}
+
+// Runs the block stack over the pass's rows.  On return ws.h holds the
+// residual after the last execution and, when the model has a vocabulary,
+// ws.x the final-normed rows.  cap_row0 / cap_rows place these rows in the
+// capture buffer.
+void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, int cap_row0,
+               int cap_rows) {
+  llama_model* m = p.m;
+  const Dims& d = m->d;
+  const llama_config& c = m->cfg;
+  const int rows = p.nseq * p.rows_per_seq;
+  uint16_t* h = m->at<uint16_t>(m->L.h);
+  uint16_t* x = m->at<uint16_t>(m->L.x);
+  uint16_t* qkv = m->at<uint16_t>(m->L.qkv);
+  uint16_t* q = m->at<uint16_t>(m->L.q);
+  uint16_t* att = m->at<uint16_t>(m->L.att);
+  uint16_t* mm = m->at<uint16_t>(m->L.m);
+  float* part = m->at<float>(m->L.part);
+  const size_t rowb = (size_t)d.H * 2;
+
+  if (tok) launch_embed(m->embed, d.V, d.H, tok, h, rows, p.s);
+  else (void)hipMemcpyAsync(h, hin, rows * rowb, hipMemcpyDeviceToDevice, p.s);
+
+  for (int loop = 0; loop < c.n_loops; ++loop) {
+    for (int b = 0; b < c.n_blocks; ++b) {
+      const int e = loop * c.n_blocks + b;
+      const llama_block_weights& w = m->blocks[b];
+      RowTable tab = table_for(p, e);
+
+      launch_rmsnorm(h, w.attn_norm, x, rows, d.H, c.rms_eps, p.s);
+      GemvSeg qkvseg[3] = {{(const uint16_t*)w.q, 0, d.qd},
+                           {(const uint16_t*)w.k, d.qd, d.qd + d.kvd},
+                           {(const uint16_t*)w.v, d.qd + d.kvd, d.qd + 2 * d.kvd}};
+      const int nqkv = d.qd + 2 * d.kvd;
+      {
+        Timed t(m, LLAMA_TIMING_QKV, p.s);
+        gemv_rows(GEMV_STORE, qkvseg, 3, nqkv, d.H, x, d.H, rows, qkv, nqkv, nullptr, 0, p.s);
+      }
+      launch_rope_kv(qkv, q, tab, rows, d.nq, d.nkv, d.d, (float)c.rope_theta, p.s);
+      {
+        Timed t(m, LLAMA_TIMING_ATTN, p.s);
+        launch_attn_decode(q, tab, rows, d.nq, d.nkv, d.d, part, d.max_blocks, att, p.s);
+      }
+      GemvSeg oseg[1] = {{(const uint16_t*)w.o, 0, d.H}};
+      {
+        Timed t(m, LLAMA_TIMING_O, p.s);
+        gemv_rows(GEMV_RESIDUAL, oseg, 1, d.H, d.qd, att, d.qd, rows, h, d.H, nullptr, 0, p.s);
+      }
+      if (m->cap)
+        (void)hipMemcpy2DAsync((uint8_t*)m->cap + (((size_t)e * 2 + 0) * cap_rows + cap_row0) * rowb,
+                         rowb, h, rowb, rowb, rows, hipMemcpyDeviceToDevice, p.s);
+
+      launch_rmsnorm(h, w.mlp_norm, x, rows, d.H, c.rms_eps, p.s);
+      GemvSeg gu[2] = {{(const uint16_t*)w.gate, 0, d.F}, {(const uint16_t*)w.up, 0, d.F}};
+      {
+        Timed t(m, LLAMA_TIMING_GATE_UP, p.s);
+        gemv_rows(GEMV_SWIGLU, gu, 2, d.F, d.H, x, d.H, rows, mm, d.F, nullptr, 0, p.s);
+      }
+      GemvSeg dseg[1] = {{(const uint16_t*)w.down, 0, d.H}};
+      {
+        Timed t(m, LLAMA_TIMING_DOWN, p.s);
+        gemv_rows(GEMV_RESIDUAL, dseg, 1, d.H, d.F, mm, d.F, rows, h, d.H, nullptr, 0, p.s);
+      }
+      if (m->cap)
+        (void)hipMemcpy2DAsync((uint8_t*)m->cap + (((size_t)e * 2 + 1) * cap_rows + cap_row0) * rowb,
+                         rowb, h, rowb, rowb, rows, hipMemcpyDeviceToDevice, p.s);
+    }
+    const bool last = loop == c.n_loops - 1;
+    if (last && hout) (void)hipMemcpyAsync(hout, h, rows * rowb, hipMemcpyDeviceToDevice, p.s);
+    if (d.V) {
+      // final norm at the end of every loop; it replaces the residual between loops
+      launch_rmsnorm(h, m->final_norm, last ? x : h, rows, d.H, c.rms_eps, p.s);
+    }
+  }
+}
+
+// lm_head over `rows` final-normed rows starting at x, then the greedy draw.
+void run_head(llama_model* m, const uint16_t* x, int rows, void* logits_bf16, float* logits_f32,
+              int32_t* next, hipStream_t s) {
+  const Dims& d = m->d;
+  GemvSeg seg[1] = {{(const uint16_t*)m->lm_head, 0, d.V}};
+  for (int r0 = 0; r0 < rows; r0 += d.Llog) {
+    int n = std::min(d.Llog, rows - r0);
+    uint16_t* lb = logits_bf16 ? (uint16_t*)logits_bf16 + (size_t)r0 * d.V
+                               : m->at<uint16_t>(m->L.logits);
+    {
+      Timed t(m, LLAMA_TIMING_LM_HEAD, s);
+      gemv_rows(GEMV_STORE, seg, 1, d.V, d.H, x + (size_t)r0 * d.H, d.H, n, lb, d.V,
+                logits_f32 ? logits_f32 + (size_t)r0 * d.V : nullptr, d.V, s);
+    }
+    if (next)
+      launch_argmax(lb, d.V, d.V, n, m->at<float>(m->L.amx_v), m->at<int>(m->L.amx_i), next + r0,
+                    m->at<int>(m->L.flag), s);
+  }
+}
+
+// The first step on a model clears its non-finite flag (a fill kernel, so the
+// clearing can sit inside a captured graph).
+void ready_flag(llama_model* m, hipStream_t s) {
+  if (!m->flag_ready) {
+    launch_fill_zero(m->at<int>(m->L.flag), 64, s);
+    m->flag_ready = true;
+  }
+}
+
+int check_kv(const llama_model* m, const llama_kv* kv) {
+  if (!kv) return fail(LLAMA_E_ARG, "cache handle is NULL");
+  if (kv->model != m) return fail(LLAMA_E_ARG, "cache belongs to another model");
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t llama_workspace_bytes(const llama_config* cfg, int32_t max_positions) {
+  if (check_config(cfg) != LLAMA_OK || max_positions < 1) return 0;
+  return layout_of(dims_of(*cfg, max_positions)).total;
+}
+
+int llama_load_weights(const llama_config* cfg, const llama_block_weights* blocks,
+                       const void* embed, const void* final_norm, const void* lm_head,
+                       void* workspace_dev, size_t workspace_bytes, int32_t max_positions,
+                       llama_model** out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(LLAMA_E_ARG, "out is NULL");
+  if (!blocks) return fail(LLAMA_E_ARG, "blocks is NULL");
+  if (max_positions < 1) return fail(LLAMA_E_ARG, "max_positions must be positive");
+  for (int b = 0; b < cfg->n_blocks; ++b) {
+    const llama_block_weights& w = blocks[b];
+    if (!w.attn_norm || !w.q || !w.k || !w.v || !w.o || !w.mlp_norm || !w.gate || !w.up || !w.down)
+      return fail(LLAMA_E_ARG, "block %d has a NULL weight", b);
+  }
+  if (cfg->vocab) {
+    if (!embed || !final_norm || !lm_head)
+      return fail(LLAMA_E_ARG, "embed, final_norm and lm_head are required with a vocabulary");
+    if (lm_head == embed)
+      return fail(LLAMA_E_GEOMETRY, "tied heads are refused: lm_head is the embedding");
+  } else if (embed || final_norm || lm_head) {
+    return fail(LLAMA_E_ARG, "a blocks-only model (vocab 0) takes no embed/final_norm/lm_head");
+  }
+  Dims d = dims_of(*cfg, max_positions);
+  Layout L = layout_of(d);
+  if (!workspace_dev) return fail(LLAMA_E_ARG, "workspace is NULL");
+  if (workspace_bytes < L.total)
+    return fail(LLAMA_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  llama_model* m = new llama_model();
+  m->cfg = *cfg;
+  m->d = d;
+  m->L = L;
+  m->blocks.assign(blocks, blocks + cfg->n_blocks);
+  m->embed = embed;
+  m->final_norm = final_norm;
+  m->lm_head = lm_head;
+  m->ws = (uint8_t*)workspace_dev;
+  m->max_positions = max_positions;
+  m->cap = nullptr;
+  m->cap_bytes = 0;
+  m->flag_ready = false;
+  *out = m;
+  g_err.clear();
+  return LLAMA_OK;
+}
+
+size_t llama_kv_bytes(const llama_model* m, int32_t max_positions) {
+  if (!m || max_positions < 1) return 0;
+  return (size_t)m->d.nexec * max_positions * m->d.kvd * 2 * 2;
+}
+
+int llama_kv_alloc(llama_model* m, int32_t max_positions, void* device_buf, size_t bytes,
+                   llama_kv** out) {
+  if (!m || !out || !device_buf) return fail(LLAMA_E_ARG, "NULL argument");
+  if (max_positions < 1 || max_positions > m->max_positions)
+    return fail(LLAMA_E_CAPACITY, "max_positions %d outside 1..%d", max_positions,
+                m->max_positions);
+  size_t need = llama_kv_bytes(m, max_positions);
+  if (bytes < need) return fail(LLAMA_E_WORKSPACE, "cache of %zu bytes, %zu needed", bytes, need);
+  llama_kv* kv = new llama_kv();
+  kv->model = m;
+  kv->buf = (uint8_t*)device_buf;
+  kv->max_positions = max_positions;
+  kv->length = 0;
+  kv->slab = (size_t)max_positions * m->d.kvd * 2;
+  *out = kv;
+  return LLAMA_OK;
+}
+
+int32_t llama_kv_length(const llama_kv* kv) { return kv ? kv->length : -1; }
+
+int llama_kv_set_length(llama_kv* kv, int32_t n) {
+  if (!kv) return fail(LLAMA_E_ARG, "cache handle is NULL");
+  if (n < 0 || n > kv->max_positions)
+    return fail(LLAMA_E_CAPACITY, "length %d outside 0..%d", n, kv->max_positions);
+  kv->length = n;
+  return LLAMA_OK;
+}
+
+void* llama_kv_slab(const llama_kv* kv, int32_t exec, int32_t which) {
+  if (!kv || exec < 0 || exec >= kv->model->d.nexec || (which != 0 && which != 1)) return nullptr;
+  return kv->buf + ((size_t)exec * 2 + which) * kv->slab;
+}
+
+int llama_set_capture(llama_model* m, void* buf, size_t bytes) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  m->cap = buf;
+  m->cap_bytes = buf ? bytes : 0;
+  return LLAMA_OK;
+}
+
+static int check_capture(llama_model* m, int rows) {
+  if (!m->cap) return LLAMA_OK;
+  size_t need = (size_t)m->d.nexec * 2 * rows * m->d.H * 2;
+  if (m->cap_bytes < need)
+    return fail(LLAMA_E_WORKSPACE, "capture buffer of %zu bytes, %zu needed", m->cap_bytes, need);
+  return LLAMA_OK;
+}
+
+int llama_prefill_chunk(llama_model* m, llama_kv* kv, const int32_t* tokens_dev,
+                        const void* hidden_in_dev, int32_t n_rows, int32_t pos0,
+                        void* hidden_out_dev, void* logits_bf16_dev, float* logits_f32_dev,
+                        int32_t all_rows, int32_t* next_token_dev, void* hip_stream) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  int rc = check_kv(m, kv);
+  if (rc) return rc;
+  if (n_rows < 1 || n_rows > m->cfg.max_chunk_rows)
+    return fail(LLAMA_E_ARG, "n_rows %d outside 1..%d", n_rows, m->cfg.max_chunk_rows);
+  if (pos0 != kv->length)
+    return fail(LLAMA_E_POSITION, "pos0 %d differs from the cache length %d", pos0, kv->length);
+  if ((int64_t)pos0 + n_rows > kv->max_positions)
+    return fail(LLAMA_E_CAPACITY, "positions %d..%d pass the cache's %d", pos0, pos0 + n_rows - 1,
+                kv->max_positions);
+  if (m->d.V) {
+    if (!tokens_dev || hidden_in_dev) return fail(LLAMA_E_ARG, "a vocabulary model takes tokens");
+  } else {
+    if (tokens_dev || !hidden_in_dev) return fail(LLAMA_E_ARG, "a blocks-only model takes hidden rows");
+    if (logits_bf16_dev || logits_f32_dev || next_token_dev)
+      return fail(LLAMA_E_ARG, "a blocks-only model has no logits");
+  }
+  rc = check_capture(m, n_rows);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)hip_stream;
+  ready_flag(m, s);
+  const int W = 16;  // rows per pass
+  const size_t rowb = (size_t)m->d.H * 2;
+  for (int r0 = 0; r0 < n_rows; r0 += W) {
+    int n = std::min(W, n_rows - r0);
+    Pass p{m, &kv, 1, n, {0}, s};
+    p.pos0[0] = pos0 + r0;
+    run_stack(p, tokens_dev ? tokens_dev + r0 : nullptr,
+              hidden_in_dev ? (const uint8_t*)hidden_in_dev + r0 * rowb : nullptr,
+              hidden_out_dev ? (uint8_t*)hidden_out_dev + r0 * rowb : nullptr, r0, n_rows);
+    if (m->d.V) {
+      const uint16_t* x = m->at<uint16_t>(m->L.x);
+      if (all_rows) {
+        run_head(m, x, n, logits_bf16_dev ? (uint16_t*)logits_bf16_dev + (size_t)r0 * m->d.V : nullptr,
+                 logits_f32_dev ? logits_f32_dev + (size_t)r0 * m->d.V : nullptr,
+                 next_token_dev ? next_token_dev + r0 : nullptr, s);
+      } else if (r0 + n == n_rows) {
+        run_head(m, x + (size_t)(n - 1) * m->d.H, 1, logits_bf16_dev, logits_f32_dev,
+                 next_token_dev, s);
+      }
+    }
+  }
+  rc = dev_check("prefill launch");
+  if (rc) return rc;
+  kv->length += n_rows;
+  return LLAMA_OK;
+}
+
+int llama_decode_step(llama_model* m, llama_kv* const* kvs, int32_t n_seq,
+                      const int32_t* tokens_dev, const void* hidden_in_dev, int32_t rows,
+                      void* hidden_out_dev, void* logits_bf16_dev, float* logits_f32_dev,
+                      int32_t* next_tokens_dev, void* hip_stream) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  if (!kvs) return fail(LLAMA_E_ARG, "kvs is NULL");
+  if (n_seq < 1 || n_seq > m->cfg.max_seqs)
+    return fail(LLAMA_E_ARG, "n_seq %d outside 1..%d", n_seq, m->cfg.max_seqs);
+  if (rows < 1 || rows > m->cfg.max_window_rows)
+    return fail(LLAMA_E_ARG, "rows %d outside 1..%d", rows, m->cfg.max_window_rows);
+  for (int i = 0; i < n_seq; ++i) {
+    int rc = check_kv(m, kvs[i]);
+    if (rc) return rc;
+    for (int j = 0; j < i; ++j)
+      if (kvs[j] == kvs[i]) return fail(LLAMA_E_ARG, "sequence %d repeats sequence %d's cache", i, j);
+    if ((int64_t)kvs[i]->length + rows > kvs[i]->max_positions)
+      return fail(LLAMA_E_CAPACITY, "sequence %d: positions %d..%d pass the cache's %d", i,
+                  kvs[i]->length, kvs[i]->length + rows - 1, kvs[i]->max_positions);
+  }
+  if (m->d.V) {
+    if (!tokens_dev || hidden_in_dev) return fail(LLAMA_E_ARG, "a vocabulary model takes tokens");
+  } else {
+    if (tokens_dev || !hidden_in_dev) return fail(LLAMA_E_ARG, "a blocks-only model takes hidden rows");
+    if (logits_bf16_dev || logits_f32_dev || next_tokens_dev)
+      return fail(LLAMA_E_ARG, "a blocks-only model has no logits");
+  }
+  const int total = n_seq * rows;
+  int rc = check_capture(m, total);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)hip_stream;
+  ready_flag(m, s);
+  Pass p{m, kvs, n_seq, rows, {0}, s};
+  for (int i = 0; i < n_seq; ++i) p.pos0[i] = kvs[i]->length;
+  run_stack(p, tokens_dev, hidden_in_dev, hidden_out_dev, 0, total);
+  if (m->d.V && (logits_bf16_dev || logits_f32_dev || next_tokens_dev))
+    run_head(m, m->at<uint16_t>(m->L.x), total, logits_bf16_dev, logits_f32_dev, next_tokens_dev,
+             s);
+  rc = dev_check("decode launch");
+  if (rc) return rc;
+  for (int i = 0; i < n_seq; ++i) kvs[i]->length += rows;
+  return LLAMA_OK;
+}
+
+int llama_check_finite(llama_model* m, void* hip_stream) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  hipStream_t s = (hipStream_t)hip_stream;
+  int flag = 0;
+  if (hipMemcpyAsync(&flag, m->ws + m->L.flag, sizeof(int), hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(LLAMA_E_DEVICE, "reading the non-finite flag failed");
+  if (flag) {
+    launch_fill_zero(m->at<int>(m->L.flag), 64, s);
+    (void)hipStreamSynchronize(s);
+    return fail(LLAMA_E_NONFINITE, "a greedy draw met a logit row holding NaN or Inf");
+  }
+  return LLAMA_OK;
+}
+
+static void release_timing(llama_model* m) {
+  for (hipEvent_t e : m->tev) (void)hipEventDestroy(e);
+  m->tev.clear();
+  m->tused = 0;
+  m->timing_kernel = 0;
+}
+
+int llama_set_timing(llama_model* m, int32_t kernel, int32_t max_launches) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  if (kernel < LLAMA_TIMING_OFF || kernel > LLAMA_TIMING_PREFILL_ATTN)
+    return fail(LLAMA_E_ARG, "unknown kernel class %d", kernel);
+  release_timing(m);
+  if (kernel == LLAMA_TIMING_OFF) return LLAMA_OK;
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(LLAMA_E_ARG, "max_launches %d outside 1..2^20", max_launches);
+  m->tev.resize((size_t)max_launches * 2);
+  for (auto& e : m->tev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      release_timing(m);
+      return fail(LLAMA_E_DEVICE, "hipEventCreate failed");
+    }
+  }
+  m->timing_kernel = kernel;
+  return LLAMA_OK;
+}
+
+int llama_timing_read(llama_model* m, double* total_ms, int64_t* launches) {
+  if (!m || !total_ms || !launches) return fail(LLAMA_E_ARG, "NULL argument");
+  double sum = 0.0;
+  for (size_t i = 0; i + 1 < m->tused; i += 2) {
+    float ms = 0.f;
+    if (hipEventSynchronize(m->tev[i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, m->tev[i], m->tev[i + 1]) != hipSuccess)
+      return fail(LLAMA_E_DEVICE, "reading timing events failed");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)(m->tused / 2);
+  m->tused = 0;
+  return LLAMA_OK;
+}
+
+void llama_kv_free(llama_kv* kv) { delete kv; }
+void llama_free(llama_model* m) {
+  if (m) release_timing(m);
+  delete m;
+}
+const char* llama_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

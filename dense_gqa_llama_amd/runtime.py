@@ -1,0 +1,149 @@
+"""PyTorch-side handles: device memory for the workspace and caches, and
+calls into the C ABI on the current stream.  Marshalling only."""
+import torch
+
+from . import binding as B
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Model:
+    """Wraps llama_load_weights.  ``weights`` maps names to bf16 device
+    tensors: ``embed``, ``final_norm``, ``lm_head`` (absent for a blocks-only
+    model) and ``b{i}.{attn_norm,q,k,v,o,mlp_norm,gate,up,down}``."""
+
+    def __init__(self, geom, weights, max_positions, max_chunk_rows=2048, max_window_rows=16,
+                 max_seqs=2, device="cuda"):
+        self.g = geom
+        self.cfg = B.make_config(geom.n_blocks, geom.n_loops, geom.hidden, geom.n_q_heads,
+                                 geom.n_kv_heads, geom.head_dim, geom.ffn, geom.vocab,
+                                 geom.rope_theta, geom.rms_eps, max_chunk_rows, max_window_rows,
+                                 max_seqs)
+        self.max_positions = max_positions
+        nbytes = B.llama_workspace_bytes(self.cfg, max_positions)
+        if nbytes == 0:
+            raise B.LlamaError(B.LLAMA_E_GEOMETRY, B.last_error())
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.weights = weights
+        blocks = [{f: weights[f"b{i}.{f}"].data_ptr() for f in B.BLOCK_FIELDS}
+                  for i in range(geom.n_blocks)]
+        get = lambda k: weights[k].data_ptr() if k in weights else None  # noqa: E731
+        self.handle = B.llama_load_weights(self.cfg, blocks, get("embed"), get("final_norm"),
+                                           get("lm_head"), self.workspace.data_ptr(), nbytes,
+                                           max_positions)
+        self.capture = None
+
+    def new_sequence(self, max_positions=None):
+        return Sequence(self, max_positions or self.max_positions)
+
+    def set_capture(self, rows):
+        """Allocates and installs a capture buffer for steps of ``rows`` rows
+        (bf16 [executions][2][rows][hidden]); ``rows=0`` clears it."""
+        if not rows:
+            B.llama_set_capture(self.handle, None, 0)
+            self.capture = None
+            return None
+        g = self.g
+        self.capture = torch.empty((g.n_blocks * g.n_loops, 2, rows, g.hidden), dtype=torch.int16,
+                                   device=self.workspace.device)
+        B.llama_set_capture(self.handle, self.capture.data_ptr(),
+                            self.capture.numel() * 2)
+        return self.capture
+
+    def prefill(self, seq, tokens=None, hidden=None, all_rows=False, want_logits=True,
+                want_hidden=False):
+        """One prompt chunk.  Returns dict of device tensors: ``next`` (int32),
+        and when asked ``logits`` (bf16 bits as int16), ``logits32``, ``hidden``."""
+        g = self.g
+        n = (tokens if tokens is not None else hidden).shape[0]
+        dev = self.workspace.device
+        nl = n if all_rows else 1
+        out = {}
+        if g.vocab:
+            out["next"] = torch.empty(nl, dtype=torch.int32, device=dev)
+            if want_logits:
+                out["logits"] = torch.empty((nl, g.vocab), dtype=torch.int16, device=dev)
+                out["logits32"] = torch.empty((nl, g.vocab), dtype=torch.float32, device=dev)
+        if want_hidden or not g.vocab:
+            out["hidden"] = torch.empty((n, g.hidden), dtype=torch.int16, device=dev)
+        B.llama_prefill_chunk(self.handle, seq.handle, _ptr(tokens), _ptr(hidden), n, seq.length,
+                              _ptr(out.get("hidden")), _ptr(out.get("logits")),
+                              _ptr(out.get("logits32")), int(all_rows), _ptr(out.get("next")),
+                              _stream())
+        return out
+
+    def decode(self, seqs, tokens=None, hidden=None, rows=1, want_logits=True, want_hidden=False,
+               next_out=None):
+        """One decode window for each sequence in ``seqs`` (batched).
+        tokens: int32 [n_seq*rows]; returns dict as :meth:`prefill`."""
+        g = self.g
+        total = len(seqs) * rows
+        dev = self.workspace.device
+        out = {}
+        if g.vocab:
+            out["next"] = next_out if next_out is not None else torch.empty(
+                total, dtype=torch.int32, device=dev)
+            if want_logits:
+                out["logits"] = torch.empty((total, g.vocab), dtype=torch.int16, device=dev)
+                out["logits32"] = torch.empty((total, g.vocab), dtype=torch.float32, device=dev)
+        if want_hidden or not g.vocab:
+            out["hidden"] = torch.empty((total, g.hidden), dtype=torch.int16, device=dev)
+        B.llama_decode_step(self.handle, [s.handle for s in seqs], _ptr(tokens), _ptr(hidden),
+                            rows, _ptr(out.get("hidden")), _ptr(out.get("logits")),
+                            _ptr(out.get("logits32")), _ptr(out.get("next")), _stream())
+        return out
+
+    def check_finite(self):
+        B.llama_check_finite(self.handle, _stream())
+
+    def close(self):
+        if self.handle:
+            B.llama_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Sequence:
+    """One sequence's cache (every execution), in a caller-owned device buffer."""
+
+    def __init__(self, model, max_positions):
+        self.model = model
+        nbytes = B.llama_kv_bytes(model.handle, max_positions)
+        g = model.g
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=model.workspace.device)
+        self.handle = B.llama_kv_alloc(model.handle, max_positions, self.buf.data_ptr(), nbytes)
+        self.max_positions = max_positions
+        self.shape = (g.n_blocks * g.n_loops, 2, max_positions, g.n_kv_heads, g.head_dim)
+
+    @property
+    def length(self):
+        return B.llama_kv_length(self.handle)
+
+    def set_length(self, n):
+        B.llama_kv_set_length(self.handle, n)
+
+    def view(self):
+        """The cache as int16 [executions][K/V][positions][kv_heads][head_dim]."""
+        return self.buf.view(torch.int16).view(self.shape)
+
+    def close(self):
+        if self.handle:
+            B.llama_kv_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

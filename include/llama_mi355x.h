@@ -1,0 +1,194 @@
+/* llama_mi355x.h -- C ABI of the MI355X (gfx950) forward step of a dense
+ * grouped-query Llama decoder served from bf16 weights with a bf16
+ * position-major key/value cache.
+ *
+ * The step is Hugging Face modeling_llama in bf16 at its rounding points, as
+ * the pull request "llama: Nanbeige4.3-33B on Metal, the bf16 release served
+ * as published" states them (section "How"): each residual add rounded to
+ * bf16; RMSNorm bf16(w * bf16(x * rsqrt(mean(x^2) + eps))); RoPE
+ * bf16(bf16(x c) + bf16(rot(x) s)) with bf16 cos and sin of the fp32 angle;
+ * SwiGLU bf16(bf16(silu(g)) * u); row projections with fp32 sums rounded
+ * once.  Attention scores, softmax and the weighted sum of values are fp32
+ * and the attention output is rounded once.  Greedy tokens are drawn on the
+ * GPU, ties to the lower id (review reply "Teacher-forced misses").
+ *
+ * Memory.  Every pointer named *_dev, every weight and the workspace and
+ * cache buffers are device addresses owned by the caller; the library only
+ * borrows them and they must outlive the handles that hold them.  Handles are
+ * host objects freed by llama_free / llama_kv_free.  No call allocates device
+ * memory.
+ *
+ * Layouts.  bf16 values are 16-bit patterns.  Projection weights are
+ * [out][in] row-major, as published: q [n_q_heads*head_dim][hidden],
+ * k and v [n_kv_heads*head_dim][hidden], o [hidden][n_q_heads*head_dim],
+ * gate and up [ffn][hidden], down [hidden][ffn], embed and lm_head
+ * [vocab][hidden]; norm weights [hidden].  Activations are [row][width].
+ * The cache of one sequence holds, for every execution e (block b of loop l
+ * is e = l*n_blocks + b), keys then values, each [max_positions][n_kv_heads]
+ * [head_dim] with position p at slot p (keys after RoPE).
+ *
+ * Asynchrony and errors.  Every call validates its arguments on the host
+ * before it enqueues anything on `hip_stream` (a hipStream_t; NULL is the
+ * default stream) and returns without blocking.  On a refusal it returns a
+ * negative LLAMA_E_* code, changes no state, and llama_last_error() (per
+ * thread) names the reason.  A launch failure reports LLAMA_E_DEVICE.
+ * Cache lengths advance on the host when a step is enqueued.
+ */
+#ifndef LLAMA_MI355X_H
+#define LLAMA_MI355X_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LLAMA_OK = 0,
+  LLAMA_E_ARG = -1,        /* NULL or inconsistent argument */
+  LLAMA_E_GEOMETRY = -2,   /* geometry the kernels do not serve (refused at load) */
+  LLAMA_E_CAPACITY = -3,   /* a position would reach past the cache */
+  LLAMA_E_POSITION = -4,   /* pos0 differs from the cache length */
+  LLAMA_E_DEVICE = -5,     /* a HIP call or launch failed */
+  LLAMA_E_NONFINITE = -6,  /* a logit row held NaN or +-Inf */
+  LLAMA_E_WORKSPACE = -7   /* workspace or buffer smaller than required */
+};
+
+/* Geometry.  Served set (others are refused with LLAMA_E_GEOMETRY):
+ * head_dim 64 or 128; hidden, ffn, n_q_heads*head_dim, n_kv_heads*head_dim
+ * and vocab multiples of 128; n_q_heads a multiple of n_kv_heads with at
+ * most 8 query heads per KV head; rope_theta > 0; vocab 0 means a model of
+ * blocks only (no embedding, final norm or lm_head: rows enter and leave as
+ * hidden states).  The final norm, when present, is applied at the end of
+ * every loop (the looped architecture of the Nanbeige4.2-3B card, section
+ * "About the architecture"). */
+typedef struct {
+  int32_t n_blocks;        /* blocks with their own weights */
+  int32_t n_loops;         /* passes over the block stack per step (>= 1) */
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn;
+  int32_t vocab;           /* 0: blocks only */
+  double rope_theta;       /* unscaled RoPE base */
+  float rms_eps;
+  int32_t max_chunk_rows;  /* largest llama_prefill_chunk, 1..2048 */
+  int32_t max_window_rows; /* largest llama_decode_step window, 1..16 */
+  int32_t max_seqs;        /* largest n_seq of llama_decode_step, 1..16 */
+} llama_config;
+
+/* Device addresses of one block's bf16 weights. */
+typedef struct {
+  const void *attn_norm, *q, *k, *v, *o, *mlp_norm, *gate, *up, *down;
+} llama_block_weights;
+
+typedef struct llama_model llama_model; /* opaque */
+typedef struct llama_kv llama_kv;       /* opaque: one sequence, every execution */
+
+/* Bytes of device workspace a model needs for caches of up to
+ * `max_positions` positions; 0 if the configuration is refused. */
+size_t llama_workspace_bytes(const llama_config* cfg, int32_t max_positions);
+
+/* Checks the geometry and records the weight and workspace addresses.
+ * blocks[n_blocks]; embed, final_norm and lm_head must be NULL when vocab is
+ * 0 and non-NULL otherwise; a tied head (lm_head == embed) is refused, as on
+ * the pull request's "Checks" list.  Host-only: nothing is enqueued; the
+ * first step on the model initialises the workspace on its own stream.
+ * workspace_bytes must be at least llama_workspace_bytes(cfg, max_positions),
+ * and caches of this model may hold at most max_positions positions. */
+int llama_load_weights(const llama_config* cfg, const llama_block_weights* blocks,
+                       const void* embed, const void* final_norm, const void* lm_head,
+                       void* workspace_dev, size_t workspace_bytes, int32_t max_positions,
+                       llama_model** out);
+
+/* Cache bytes for one sequence of up to max_positions positions:
+ * executions * max_positions * n_kv_heads * head_dim * 2 (K, V) * 2 bytes. */
+size_t llama_kv_bytes(const llama_model* model, int32_t max_positions);
+
+/* Wraps a caller-owned device buffer of llama_kv_bytes() bytes as an empty
+ * cache (length 0).  max_positions may not exceed the model's. */
+int llama_kv_alloc(llama_model* model, int32_t max_positions, void* device_buf, size_t bytes,
+                   llama_kv** out);
+
+int32_t llama_kv_length(const llama_kv* kv);
+
+/* Sets the cache length: shorter keeps a prefix (a resumed prompt state);
+ * longer declares positions the caller wrote into the buffer itself. */
+int llama_kv_set_length(llama_kv* kv, int32_t n_positions);
+
+/* Device address of execution e's keys (which = 0) or values (which = 1). */
+void* llama_kv_slab(const llama_kv* kv, int32_t exec, int32_t which);
+
+/* One prompt chunk of n_rows (1..max_chunk_rows) rows of one sequence at
+ * positions [pos0, pos0 + n_rows); pos0 must equal the cache length.  Rows
+ * come from tokens_dev (int32 [n_rows]) through the embedding, or, for a
+ * blocks-only model, from hidden_in_dev (bf16 [n_rows][hidden]).  Outputs,
+ * each optional (NULL): hidden_out_dev bf16 [n_rows][hidden], the residual
+ * after the last execution, before the final norm; logits_bf16_dev and
+ * logits_f32_dev ([n_rows or 1][vocab]: every row when all_rows != 0, else
+ * the last) with the fp32 sums before their rounding; next_token_dev (int32
+ * [n_rows or 1]) the greedy id of each logit row, -1 for a row holding NaN
+ * or +-Inf.  Prompt chunks of up to 2,048 rows follow the pull request's
+ * section "How". */
+int llama_prefill_chunk(llama_model* model, llama_kv* kv, const int32_t* tokens_dev,
+                        const void* hidden_in_dev, int32_t n_rows, int32_t pos0,
+                        void* hidden_out_dev, void* logits_bf16_dev, float* logits_f32_dev,
+                        int32_t all_rows, int32_t* next_token_dev, void* hip_stream);
+
+/* One decode window of `rows` (1..max_window_rows) rows for each of n_seq
+ * sequences (1..max_seqs, distinct caches), all batched into one pass: the
+ * rows of sequence s sit at positions [len_s, len_s + rows).  tokens_dev is
+ * int32 [n_seq][rows] (or hidden_in_dev bf16 [n_seq][rows][hidden] for a
+ * blocks-only model); hidden_out_dev, logits_bf16_dev, logits_f32_dev and
+ * next_tokens_dev are laid out [n_seq][rows][...], each optional.  Every row
+ * is computed exactly as a one-row step at its position would compute it, so
+ * windows equal one-row steps and batched sequences equal solo runs bit for
+ * bit (pull request, section "Measured"). */
+int llama_decode_step(llama_model* model, llama_kv* const* kvs, int32_t n_seq,
+                      const int32_t* tokens_dev, const void* hidden_in_dev, int32_t rows,
+                      void* hidden_out_dev, void* logits_bf16_dev, float* logits_f32_dev,
+                      int32_t* next_tokens_dev, void* hip_stream);
+
+/* Test hook: while set, every step also writes each execution's residuals to
+ * buf_dev as bf16 [executions][2][rows][hidden] ([0] after the attention
+ * half, [1] after the MLP half; rows = the step's total rows).  NULL clears
+ * it.  A later step whose capture would not fit is refused. */
+int llama_set_capture(llama_model* model, void* buf_dev, size_t bytes);
+
+/* Measurement hook for benchmarks.  While `kernel` is one of the classes
+ * below, every step records a HIP event pair on its own stream around each
+ * launch of that class, from a pool of max_launches pairs created by this
+ * call (host-side event objects; no device memory).  Launches beyond the pool
+ * are not recorded.  kernel = LLAMA_TIMING_OFF releases the pool.
+ * llama_timing_read synchronises on the recorded events and returns the
+ * summed milliseconds and the number of launches since the previous read. */
+enum {
+  LLAMA_TIMING_OFF = 0,
+  LLAMA_TIMING_GATE_UP = 1,   /* decode gate/up projection with SwiGLU */
+  LLAMA_TIMING_DOWN = 2,      /* decode down projection + residual */
+  LLAMA_TIMING_QKV = 3,       /* decode q/k/v projection */
+  LLAMA_TIMING_O = 4,         /* decode o projection + residual */
+  LLAMA_TIMING_LM_HEAD = 5,   /* decode lm_head projection */
+  LLAMA_TIMING_ATTN = 6,      /* decode attention, both passes */
+  LLAMA_TIMING_PREFILL_GEMM = 7, /* every prompt-chunk projection */
+  LLAMA_TIMING_PREFILL_ATTN = 8  /* prompt-chunk attention */
+};
+int llama_set_timing(llama_model* model, int32_t kernel, int32_t max_launches);
+int llama_timing_read(llama_model* model, double* total_ms, int64_t* launches);
+
+/* Synchronises hip_stream, then reports LLAMA_E_NONFINITE if any greedy
+ * draw since the last call met a non-finite logit row (and clears the
+ * flag), else LLAMA_OK. */
+int llama_check_finite(llama_model* model, void* hip_stream);
+
+void llama_kv_free(llama_kv* kv);
+void llama_free(llama_model* model);
+
+/* Reason for the calling thread's last refusal ("" if none). */
+const char* llama_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

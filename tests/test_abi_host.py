@@ -1,0 +1,157 @@
+"""The C-ABI library on the host: it loads, exports every entry point the
+header declares, sizes its buffers, and refuses bad arguments before it
+enqueues anything (so no GPU is needed).  Refusals follow the pull request
+"llama: Nanbeige4.3-33B on Metal, the bf16 release served as published"
+(tied heads and other geometries refused at load, section "Checks") and the
+NInfer card's capacity check (the position past the cache is rejected,
+section "Validation")."""
+import os
+import re
+
+import pytest
+
+from synth.workloads import CONFIGS
+
+B = pytest.importorskip("dense_gqa_llama_amd.binding")
+
+FAKE = 0x10000  # host-side stand-in address; the refusal paths never touch it
+
+
+def header_functions(root):
+    text = open(os.path.join(root, "include", "llama_mi355x.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(llama_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(root):
+    import ctypes
+    lib = ctypes.CDLL(B.LIB_PATH)
+    names = header_functions(root)
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def cfg_of(g, **kw):
+    base = dict(n_blocks=g.n_blocks, n_loops=g.n_loops, hidden=g.hidden, n_q_heads=g.n_q_heads,
+                n_kv_heads=g.n_kv_heads, head_dim=g.head_dim, ffn=g.ffn, vocab=g.vocab,
+                rope_theta=g.rope_theta, rms_eps=g.rms_eps)
+    base.update(kw)
+    extra = {k: base.pop(k) for k in ("max_chunk_rows", "max_window_rows", "max_seqs") if k in base}
+    return B.make_config(**base, **extra)
+
+
+@pytest.mark.parametrize("i", sorted(CONFIGS))
+def test_served_configs_are_sized(i):
+    g = CONFIGS[i]
+    assert B.llama_workspace_bytes(cfg_of(g), 4096) > 0
+
+
+@pytest.mark.parametrize("change", [
+    dict(head_dim=96), dict(hidden=7000), dict(n_q_heads=50), dict(n_q_heads=72, n_kv_heads=8),
+    dict(vocab=166913), dict(rope_theta=0.0), dict(max_chunk_rows=4096), dict(max_window_rows=17),
+    dict(max_seqs=0), dict(ffn=22000), dict(n_loops=0), dict(rms_eps=-1.0),
+])
+def test_refused_geometries(change):
+    g = CONFIGS[3]
+    assert B.llama_workspace_bytes(cfg_of(g, **change), 4096) == 0
+    assert B.last_error()
+
+
+def blocks(n):
+    return [{f: FAKE for f in B.BLOCK_FIELDS} for _ in range(n)]
+
+
+def load(g, **kw):
+    cfg = cfg_of(g, **kw)
+    ws = B.llama_workspace_bytes(cfg, 512)
+    emb = (FAKE, FAKE + 0x100, FAKE + 0x200) if g.vocab else (None, None, None)
+    return B.llama_load_weights(cfg, blocks(g.n_blocks), *emb, FAKE, ws, 512), cfg
+
+
+def expect(code, fn, *a, **k):
+    with pytest.raises(B.LlamaError) as e:
+        fn(*a, **k)
+    assert e.value.code == code, str(e.value)
+    assert B.last_error()
+
+
+def test_load_refusals():
+    g = CONFIGS[1]
+    cfg = cfg_of(g)
+    ws = B.llama_workspace_bytes(cfg, 512)
+    expect(B.LLAMA_E_GEOMETRY, B.llama_load_weights, cfg, blocks(2), FAKE, FAKE, FAKE, FAKE, ws,
+           512)  # tied head
+    expect(B.LLAMA_E_ARG, B.llama_load_weights, cfg, blocks(2), FAKE, FAKE, None, FAKE, ws, 512)
+    expect(B.LLAMA_E_WORKSPACE, B.llama_load_weights, cfg, blocks(2), FAKE, FAKE + 2, FAKE + 4,
+           FAKE, ws - 1, 512)
+    bad = blocks(2)
+    bad[1]["down"] = None
+    expect(B.LLAMA_E_ARG, B.llama_load_weights, cfg, bad, FAKE, FAKE + 2, FAKE + 4, FAKE, ws, 512)
+    g2 = CONFIGS[2]
+    cfg2 = cfg_of(g2)
+    ws2 = B.llama_workspace_bytes(cfg2, 512)
+    expect(B.LLAMA_E_ARG, B.llama_load_weights, cfg2, blocks(1), FAKE, None, None, FAKE, ws2, 512)
+
+
+def test_step_refusals_before_any_launch():
+    g = CONFIGS[1]
+    m, cfg = load(g, max_chunk_rows=64, max_window_rows=16, max_seqs=2)
+    try:
+        kvb = B.llama_kv_bytes(m, 128)
+        assert kvb == g.n_exec * 128 * g.kv_dim * 2 * 2
+        expect(B.LLAMA_E_CAPACITY, B.llama_kv_alloc, m, 513, FAKE, 10 ** 9)
+        expect(B.LLAMA_E_WORKSPACE, B.llama_kv_alloc, m, 128, FAKE, kvb - 1)
+        kv = B.llama_kv_alloc(m, 128, FAKE, kvb)
+        kv2 = B.llama_kv_alloc(m, 128, FAKE + kvb, kvb)
+        assert B.llama_kv_length(kv) == 0
+        slab = B.llama_kv_slab(kv, 1, 1)
+        assert slab == FAKE + (2 * 1 + 1) * 128 * g.kv_dim * 2
+        assert B.llama_kv_slab(kv, 2, 0) is None
+        # windows and batches
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], FAKE, None, 17)
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], FAKE, None, 0)
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv, kv], FAKE, None, 1)
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv, kv2, kv], FAKE, None, 1)
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], None, FAKE, 1)  # hidden into a vocab model
+        # capacity: the last legal position is usable, the next is refused
+        B.llama_kv_set_length(kv, 127)
+        expect(B.LLAMA_E_CAPACITY, B.llama_decode_step, m, [kv], FAKE, None, 2)
+        B.llama_kv_set_length(kv, 128)
+        expect(B.LLAMA_E_CAPACITY, B.llama_decode_step, m, [kv], FAKE, None, 1)
+        expect(B.LLAMA_E_CAPACITY, B.llama_kv_set_length, kv, 129)
+        assert B.llama_kv_length(kv) == 128  # refusal changed nothing
+        B.llama_kv_set_length(kv, 0)
+        # prompt chunks
+        expect(B.LLAMA_E_POSITION, B.llama_prefill_chunk, m, kv, FAKE, None, 8, 3)
+        expect(B.LLAMA_E_ARG, B.llama_prefill_chunk, m, kv, FAKE, None, 65, 0)
+        expect(B.LLAMA_E_ARG, B.llama_prefill_chunk, m, kv, None, None, 8, 0)
+        B.llama_kv_set_length(kv, 100)
+        expect(B.LLAMA_E_CAPACITY, B.llama_prefill_chunk, m, kv, FAKE, None, 64, 100)
+        # capture too small for the step
+        B.llama_set_capture(m, FAKE, 16)
+        B.llama_kv_set_length(kv, 0)
+        expect(B.LLAMA_E_WORKSPACE, B.llama_decode_step, m, [kv], FAKE, None, 1)
+        B.llama_set_capture(m, None, 0)
+        # another model's cache
+        m2, _ = load(g, max_chunk_rows=64)
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m2, [kv], FAKE, None, 1)
+        B.llama_free(m2)
+        B.llama_kv_free(kv)
+        B.llama_kv_free(kv2)
+    finally:
+        B.llama_free(m)
+
+
+def test_blocks_only_model_refuses_tokens_and_logits():
+    g = CONFIGS[2]
+    m, cfg = load(g, max_chunk_rows=16, max_window_rows=16, max_seqs=1)
+    try:
+        kv = B.llama_kv_alloc(m, 64, FAKE, B.llama_kv_bytes(m, 64))
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], FAKE, None, 1)
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], None, FAKE, 1, logits_bf16=FAKE)
+        expect(B.LLAMA_E_ARG, B.llama_prefill_chunk, m, kv, None, FAKE, 4, 0, next_token=FAKE)
+        B.llama_kv_free(kv)
+    finally:
+        B.llama_free(m)

@@ -80,7 +80,20 @@ _SIGS = {
 EXPORTS = tuple(_SIGS)
 
 
+def _share_torch_runtime():
+    """PyTorch ships its own HIP runtime (same SONAME, libamdhip64.so.7).  If
+    this library were loaded first it would pull in the system copy and torch
+    would later load a second runtime instance, which then owns the device.
+    Importing torch first makes the dynamic loader bind this library to the
+    runtime torch uses, so device memory and streams are shared."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def _load():
+    _share_torch_runtime()
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(LIB_PATH)

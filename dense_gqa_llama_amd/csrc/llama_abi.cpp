@@ -306,7 +306,10 @@ void run_head(llama_model* m, const uint16_t* x, int rows, void* logits_bf16, fl
 
 // The first step on a model clears its non-finite flag (a fill kernel, so the
 // clearing can sit inside a captured graph).
+// It also clears any error an unrelated earlier runtime call left behind, so
+// that the check after the step's launches reports the step's own.
 void ready_flag(llama_model* m, hipStream_t s) {
+  (void)hipGetLastError();
   if (!m->flag_ready) {
     launch_fill_zero(m->at<int>(m->L.flag), 64, s);
     m->flag_ready = true;

@@ -44,6 +44,9 @@ def _load_host():
 def _load_dev():
     global _dev
     if _dev is None:
+        # bind to the HIP runtime PyTorch already loaded (see
+        # dense_gqa_llama_amd.binding) rather than a second system copy
+        import torch  # noqa: F401
         path = os.path.join(_HERE, "libsynth_dev.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")

@@ -1,5 +1,6 @@
-"""Comparators for parity checks: bf16 step distances, the teacher-forced
-near-tie judge, the exact row comparator, and logit statistics.
+"""Comparators for parity checks: bf16 step distances (plain, and at the
+larger addend of a residual add), the teacher-forced near-tie judge, the exact
+row comparator, and logit statistics.
 
 The near-tie rule follows the pull request "llama: Nanbeige4.3-33B on Metal,
 the bf16 release served as published", review reply "Teacher-forced misses":
@@ -113,8 +114,29 @@ def mean_kl(ref_logits, test_logits):
 
 
 def within_ulps(a_bits, b_bits, ulps=2.0):
-    """Fraction of elements within `ulps` bf16 steps."""
+    """Fraction of elements within `ulps` bf16 steps (at max(|a|, |b|))."""
     d = ulp_distance(a_bits, b_bits)
+    return float((d <= ulps).mean()), float(d.max()) if d.size else 0.0
+
+
+def addend_ulps(got_bits, ref_bits, h_in_bits):
+    """Distance of residual-stream elements in bf16 steps taken at the larger
+    addend of the residual add that produced them: h_out = bf16(h_in + y) with
+    y = h_out - h_in, scale max(|got|, |ref|, |h_in|, |ref - h_in|).  A 1-step
+    difference in y moves a cancelling sum by a step of y, not of the small
+    result; measuring at the result's own magnitude would count cancellation
+    instead of error."""
+    a = bf16_bits_to_f64(got_bits)
+    b = bf16_bits_to_f64(ref_bits)
+    h = bf16_bits_to_f64(h_in_bits)
+    if not (np.isfinite(a).all() and np.isfinite(b).all()):
+        raise Refused("non-finite activation")
+    scale = np.maximum.reduce([np.abs(a), np.abs(b), np.abs(h), np.abs(b - h)])
+    return np.abs(a - b) / bf16_step(scale)
+
+
+def within_addend_ulps(got_bits, ref_bits, h_in_bits, ulps=2.0):
+    d = addend_ulps(got_bits, ref_bits, h_in_bits)
     return float((d <= ulps).mean()), float(d.max()) if d.size else 0.0
 
 

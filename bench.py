@@ -119,13 +119,15 @@ def main():
     prompt = sd.tokens(P, g.prompt_seeds[0], 0, g.vocab)
     stream = torch.cuda.current_stream()
 
-    def request():
-        """One request: prefill + D greedy steps; returns (prefill ms, decode ms)."""
+    def request(before_decode=None):
+        """One request: prefill + D greedy steps; returns its events and tokens."""
         seq.set_length(0)
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record(stream)
         out = model.prefill(seq, tokens=prompt, want_logits=False)
         e1.record(stream)
+        if before_decode:
+            before_decode()
         nxt = out["next"]
         buf = torch.empty(D, dtype=torch.int32, device="cuda")
         buf[0:1].copy_(nxt)
@@ -157,8 +159,8 @@ def main():
         f"first tokens {toks[:8]}")
 
     # dominant kernel: the decode gate/up projection (53% of a token's bytes)
-    B.llama_set_timing(model.handle, "gate_up", g.n_exec * D)
-    request()
+    # event pairs around the decode launches only (the prompt chunk is excluded)
+    request(before_decode=lambda: B.llama_set_timing(model.handle, "gate_up", g.n_exec * D))
     torch.cuda.synchronize()
     ms, n = B.llama_timing_read(model.handle)
     B.llama_set_timing(model.handle, "off")

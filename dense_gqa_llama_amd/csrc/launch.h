@@ -42,6 +42,16 @@ struct GemvSeg {
 void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* x, int ldx,
                  int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s);
 
+// Prompt-chunk projections on the matrix cores; ncols tile columns (N, or
+// 2F for SWIGLU, whose tiles interleave 32 gate and 32 up rows).
+void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* seg, int nseg,
+                 const void* gate, const void* up, void* out, int ldo, float* out32, int ld32,
+                 int ncols, hipStream_t s);
+// Prompt-chunk attention: rows at positions [pos0, pos0 + rows) against the
+// cache slabs kc / vc of one sequence.
+void launch_attn_prefill(const void* q, const void* kc, const void* vc, int rows, int pos0, int nq,
+                         int nkv, int d, void* out, hipStream_t s);
+
 // Decode attention: split over key blocks at absolute positions, then a
 // merge in block order.
 int attn_key_block();

@@ -32,7 +32,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Device workspace carved into fixed regions.
 struct Layout {
-  size_t h, x, qkv, q, att, gu, m, logits, amx_v, amx_i, part, flag, total;
+  size_t h, x, qkv, q, att, m, logits, amx_v, amx_i, part, flag, total;
 };
 
 struct Dims {
@@ -55,8 +55,7 @@ Dims dims_of(const llama_config& c, int max_positions) {
   d.V = c.vocab;
   d.nexec = c.n_blocks * c.n_loops;
   d.Mdec = c.max_seqs * c.max_window_rows;
-  // prompt chunks currently run as windows of up to 16 rows
-  d.M = std::max(d.Mdec, std::min(16, c.max_chunk_rows));
+  d.M = std::max(d.Mdec, c.max_chunk_rows);
   d.Llog = std::max(d.Mdec, 16);
   d.max_blocks = (max_positions + attn_key_block() - 1) / attn_key_block();
   return d;
@@ -75,13 +74,12 @@ Layout layout_of(const Dims& d) {
   L.qkv = take((size_t)d.M * (d.qd + 2 * d.kvd) * 2);
   L.q = take((size_t)d.M * d.qd * 2);
   L.att = take((size_t)d.M * d.qd * 2);
-  L.gu = take((size_t)d.M * 2 * d.F * 2);
   L.m = take((size_t)d.M * d.F * 2);
   int nch = d.V ? argmax_chunks(d.V) : 1;
   L.logits = take((size_t)d.Llog * std::max(d.V, 1) * 2);
   L.amx_v = take((size_t)d.Llog * nch * 4);
   L.amx_i = take((size_t)d.Llog * nch * 4);
-  L.part = take((size_t)d.M * d.nq * d.max_blocks * (d.d + 2) * 4);
+  L.part = take((size_t)d.Mdec * d.nq * d.max_blocks * (d.d + 2) * 4);
   L.flag = take(256);
   L.total = off;
   return L;
@@ -214,7 +212,7 @@ void gemv_rows(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* 
 // ws.x the final-normed rows.  cap_row0 / cap_rows place these rows in the
 // capture buffer.
 void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, int cap_row0,
-               int cap_rows) {
+               int cap_rows, bool chunk) {
   llama_model* m = p.m;
   const Dims& d = m->d;
   const llama_config& c = m->cfg;
@@ -242,19 +240,37 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
                            {(const uint16_t*)w.k, d.qd, d.qd + d.kvd},
                            {(const uint16_t*)w.v, d.qd + d.kvd, d.qd + 2 * d.kvd}};
       const int nqkv = d.qd + 2 * d.kvd;
-      {
-        Timed t(m, LLAMA_TIMING_QKV, p.s);
-        gemv_rows(GEMV_STORE, qkvseg, 3, nqkv, d.H, x, d.H, rows, qkv, nqkv, nullptr, 0, p.s);
-      }
-      launch_rope_kv(qkv, q, tab, rows, d.nq, d.nkv, d.d, (float)c.rope_theta, p.s);
-      {
-        Timed t(m, LLAMA_TIMING_ATTN, p.s);
-        launch_attn_decode(q, tab, rows, d.nq, d.nkv, d.d, part, d.max_blocks, att, p.s);
-      }
       GemvSeg oseg[1] = {{(const uint16_t*)w.o, 0, d.H}};
-      {
-        Timed t(m, LLAMA_TIMING_O, p.s);
-        gemv_rows(GEMV_RESIDUAL, oseg, 1, d.H, d.qd, att, d.qd, rows, h, d.H, nullptr, 0, p.s);
+      if (chunk) {
+        {
+          Timed t(m, LLAMA_TIMING_PREFILL_GEMM, p.s);
+          launch_gemm(GEMV_STORE, x, d.H, rows, d.H, qkvseg, 3, nullptr, nullptr, qkv, nqkv,
+                      nullptr, 0, nqkv, p.s);
+        }
+        launch_rope_kv(qkv, q, tab, rows, d.nq, d.nkv, d.d, (float)c.rope_theta, p.s);
+        {
+          Timed t(m, LLAMA_TIMING_PREFILL_ATTN, p.s);
+          launch_attn_prefill(q, tab.k[0], tab.v[0], rows, p.pos0[0], d.nq, d.nkv, d.d, att, p.s);
+        }
+        {
+          Timed t(m, LLAMA_TIMING_PREFILL_GEMM, p.s);
+          launch_gemm(GEMV_RESIDUAL, att, d.qd, rows, d.qd, oseg, 1, nullptr, nullptr, h, d.H,
+                      nullptr, 0, d.H, p.s);
+        }
+      } else {
+        {
+          Timed t(m, LLAMA_TIMING_QKV, p.s);
+          gemv_rows(GEMV_STORE, qkvseg, 3, nqkv, d.H, x, d.H, rows, qkv, nqkv, nullptr, 0, p.s);
+        }
+        launch_rope_kv(qkv, q, tab, rows, d.nq, d.nkv, d.d, (float)c.rope_theta, p.s);
+        {
+          Timed t(m, LLAMA_TIMING_ATTN, p.s);
+          launch_attn_decode(q, tab, rows, d.nq, d.nkv, d.d, part, d.max_blocks, att, p.s);
+        }
+        {
+          Timed t(m, LLAMA_TIMING_O, p.s);
+          gemv_rows(GEMV_RESIDUAL, oseg, 1, d.H, d.qd, att, d.qd, rows, h, d.H, nullptr, 0, p.s);
+        }
       }
       if (m->cap)
         (void)hipMemcpy2DAsync((uint8_t*)m->cap + (((size_t)e * 2 + 0) * cap_rows + cap_row0) * rowb,
@@ -262,14 +278,22 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
 
       launch_rmsnorm(h, w.mlp_norm, x, rows, d.H, c.rms_eps, p.s);
       GemvSeg gu[2] = {{(const uint16_t*)w.gate, 0, d.F}, {(const uint16_t*)w.up, 0, d.F}};
-      {
-        Timed t(m, LLAMA_TIMING_GATE_UP, p.s);
-        gemv_rows(GEMV_SWIGLU, gu, 2, d.F, d.H, x, d.H, rows, mm, d.F, nullptr, 0, p.s);
-      }
       GemvSeg dseg[1] = {{(const uint16_t*)w.down, 0, d.H}};
-      {
-        Timed t(m, LLAMA_TIMING_DOWN, p.s);
-        gemv_rows(GEMV_RESIDUAL, dseg, 1, d.H, d.F, mm, d.F, rows, h, d.H, nullptr, 0, p.s);
+      if (chunk) {
+        Timed t(m, LLAMA_TIMING_PREFILL_GEMM, p.s);
+        launch_gemm(GEMV_SWIGLU, x, d.H, rows, d.H, nullptr, 0, w.gate, w.up, mm, d.F, nullptr, 0,
+                    2 * d.F, p.s);
+        launch_gemm(GEMV_RESIDUAL, mm, d.F, rows, d.F, dseg, 1, nullptr, nullptr, h, d.H, nullptr,
+                    0, d.H, p.s);
+      } else {
+        {
+          Timed t(m, LLAMA_TIMING_GATE_UP, p.s);
+          gemv_rows(GEMV_SWIGLU, gu, 2, d.F, d.H, x, d.H, rows, mm, d.F, nullptr, 0, p.s);
+        }
+        {
+          Timed t(m, LLAMA_TIMING_DOWN, p.s);
+          gemv_rows(GEMV_RESIDUAL, dseg, 1, d.H, d.F, mm, d.F, rows, h, d.H, nullptr, 0, p.s);
+        }
       }
       if (m->cap)
         (void)hipMemcpy2DAsync((uint8_t*)m->cap + (((size_t)e * 2 + 1) * cap_rows + cap_row0) * rowb,
@@ -454,26 +478,16 @@ int llama_prefill_chunk(llama_model* m, llama_kv* kv, const int32_t* tokens_dev,
   if (rc) return rc;
   hipStream_t s = (hipStream_t)hip_stream;
   ready_flag(m, s);
-  const int W = 16;  // rows per pass
-  const size_t rowb = (size_t)m->d.H * 2;
-  for (int r0 = 0; r0 < n_rows; r0 += W) {
-    int n = std::min(W, n_rows - r0);
-    Pass p{m, &kv, 1, n, {0}, s};
-    p.pos0[0] = pos0 + r0;
-    run_stack(p, tokens_dev ? tokens_dev + r0 : nullptr,
-              hidden_in_dev ? (const uint8_t*)hidden_in_dev + r0 * rowb : nullptr,
-              hidden_out_dev ? (uint8_t*)hidden_out_dev + r0 * rowb : nullptr, r0, n_rows);
-    if (m->d.V) {
-      const uint16_t* x = m->at<uint16_t>(m->L.x);
-      if (all_rows) {
-        run_head(m, x, n, logits_bf16_dev ? (uint16_t*)logits_bf16_dev + (size_t)r0 * m->d.V : nullptr,
-                 logits_f32_dev ? logits_f32_dev + (size_t)r0 * m->d.V : nullptr,
-                 next_token_dev ? next_token_dev + r0 : nullptr, s);
-      } else if (r0 + n == n_rows) {
-        run_head(m, x + (size_t)(n - 1) * m->d.H, 1, logits_bf16_dev, logits_f32_dev,
-                 next_token_dev, s);
-      }
-    }
+  Pass p{m, &kv, 1, n_rows, {0}, s};
+  p.pos0[0] = pos0;
+  run_stack(p, tokens_dev, hidden_in_dev, hidden_out_dev, 0, n_rows, true);
+  if (m->d.V) {
+    const uint16_t* x = m->at<uint16_t>(m->L.x);
+    if (all_rows)
+      run_head(m, x, n_rows, logits_bf16_dev, logits_f32_dev, next_token_dev, s);
+    else
+      run_head(m, x + (size_t)(n_rows - 1) * m->d.H, 1, logits_bf16_dev, logits_f32_dev,
+               next_token_dev, s);
   }
   rc = dev_check("prefill launch");
   if (rc) return rc;
@@ -514,7 +528,7 @@ int llama_decode_step(llama_model* m, llama_kv* const* kvs, int32_t n_seq,
   ready_flag(m, s);
   Pass p{m, kvs, n_seq, rows, {0}, s};
   for (int i = 0; i < n_seq; ++i) p.pos0[i] = kvs[i]->length;
-  run_stack(p, tokens_dev, hidden_in_dev, hidden_out_dev, 0, total);
+  run_stack(p, tokens_dev, hidden_in_dev, hidden_out_dev, 0, total, false);
   if (m->d.V && (logits_bf16_dev || logits_f32_dev || next_tokens_dev))
     run_head(m, m->at<uint16_t>(m->L.x), total, logits_bf16_dev, logits_f32_dev, next_tokens_dev,
              s);

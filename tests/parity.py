@@ -76,6 +76,13 @@ def judge_row(ref, test, pos=0):
     return "near-tie"
 
 
+def top1_gate(counts, rows):
+    """Teacher-forced top-1 agreement of at least 99%, every miss a near-tie:
+    no red row, and at most max(1, 1% of rows) near-ties (on a sample of
+    under 100 positions one near-tie is the smallest possible miss)."""
+    return counts["red"] == 0 and counts["near-tie"] <= max(1, int(0.01 * rows))
+
+
 def judge(ref_rows, test_rows):
     """Judges every position; returns (counts dict, list of (pos, verdict))."""
     counts = {"equal": 0, "near-tie": 0, "red": 0}

@@ -101,7 +101,7 @@ def test_tiny_end_to_end_logits(tiny):
     assert err <= 0.05
     assert kl <= 1e-3
     assert counts["red"] == 0
-    assert counts["equal"] >= 0.99 * rows
+    assert counts["near-tie"] <= max(1, int(0.01 * rows))
     # GPU greedy ids are exactly the argmax of the GPU's own bf16 logits
     assert nxt.tolist() == [oracle.argmax(r) for r in lbf]
     # end-to-end drift of the residual stream (reported; the gate is layer-local)

@@ -56,9 +56,10 @@ class HalfRunner:
         self.zero_o = torch.zeros((g.hidden, g.q_dim), dtype=torch.int16, device="cuda")
         self.zero_down = torch.zeros((g.hidden, g.ffn), dtype=torch.int16, device="cuda")
 
-    def run(self, block, h_in, kc, vc, pos0, mode):
+    def run(self, block, h_in, kc, vc, pos0, mode, chunk=None):
         """mode: 'layer', 'attn' (down zeroed) or 'mlp' (o zeroed).  kc, vc:
         the oracle's cache of this execution (positions [0, pos0) are used).
+        chunk: run as a prompt chunk (default: when rows > 16) or a window.
         Returns (h_out bits, cache after the step as (k, v) host arrays)."""
         import dense_gqa_llama_amd as L
         w = {f"b0.{k}": self.dev[f"b{block}.{k}"] for k in KINDS}
@@ -76,10 +77,12 @@ class HalfRunner:
             v[0, 1, :pos0] = to_dev(np.ascontiguousarray(vc[:pos0]))
             s.set_length(pos0)
         hin = to_dev(np.ascontiguousarray(h_in))
-        if rows <= 16:
-            out = m.decode([s], hidden=hin, rows=rows)
-        else:
+        if chunk is None:
+            chunk = rows > 16
+        if chunk:
             out = m.prefill(s, hidden=hin)
+        else:
+            out = m.decode([s], hidden=hin, rows=rows)
         h = u16(out["hidden"])
         cache = u16(s.view())
         return h, (cache[0, 0], cache[0, 1])

@@ -1,0 +1,108 @@
+"""GPU parity at the full model sizes, sampled.  The GPU runs the launch
+configuration the benchmark times -- a whole prompt chunk (2,048 rows for the
+33B shape, 512 for the looped model) -- and, because attention is causal, its
+first rows must match the oracle's forward of those rows alone.  The oracle
+walks the blocks one at a time with weights generated on the host (as the
+float64 reference in the pull request "llama: Nanbeige4.3-33B on Metal, the
+bf16 release served as published" ran one layer's weights at a time).
+Sampled executions are also checked layer-local, per half, and a short greedy
+continuation is compared step by step."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.model import OracleModel
+from synth.workloads import config
+from tests import parity
+from tests.gpu_util import HalfRunner, exec_inputs, half_report, log, to_dev, u16
+from tests.host_inputs import HostWeights
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+SAMPLE_ROWS = 4
+DECODE = 4
+
+
+def _run(cfg, sampled_execs):
+    import dense_gqa_llama_amd as L
+    from synth import device as sd
+    g = config(cfg)
+    P = g.prompt_len
+    prompt = sd.tokens(P, g.prompt_seeds[0], 0, g.vocab)
+    ptoks = prompt.cpu().numpy()
+    # oracle: the first SAMPLE_ROWS rows, then DECODE greedy one-row steps
+    log(f"config {cfg}: oracle over {g.n_exec} executions, {SAMPLE_ROWS} rows + {DECODE} steps")
+    W = HostWeights(g, keep_blocks=1)
+    om = OracleModel(g, W)
+    oseq = om.new_sequence(SAMPLE_ROWS + DECODE)
+    r = om.forward(oseq, tokens=ptoks[:SAMPLE_ROWS], logits="all", capture=True)
+    ref64, refb, caps = r["logits64"], r["logits"], r["capture"]
+    gen = [int(r["tokens"][-1])]
+    dec64, decb = [], []
+    for _ in range(DECODE):
+        rr = om.forward(oseq, tokens=np.array([gen[-1]], dtype=np.int32), logits="all")
+        dec64.append(rr["logits64"][0])
+        decb.append(rr["logits"][0])
+        gen.append(int(rr["tokens"][-1]))
+    log(f"config {cfg}: oracle greedy {gen}")
+
+    w = sd.weights(g)
+    torch.cuda.synchronize()
+    # the benchmark's chunk: all P rows; keep the first rows' logits
+    model = L.Model(g, w, max_positions=P + DECODE, max_chunk_rows=P, max_window_rows=16,
+                    max_seqs=1)
+    seq = model.new_sequence(P + DECODE)
+    lg = torch.empty((P, g.vocab), dtype=torch.int16, device="cuda")
+    l32 = torch.empty((P, g.vocab), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(P, dtype=torch.int32, device="cuda")
+    L.binding.llama_prefill_chunk(model.handle, seq.handle, prompt.data_ptr(), None, P, 0, None,
+                                  lg.data_ptr(), l32.data_ptr(), 1, nxt.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+    got32 = l32[:SAMPLE_ROWS].cpu().numpy()
+    gotb = u16(lg[:SAMPLE_ROWS])
+    assert nxt[:SAMPLE_ROWS].cpu().tolist() == [oracle.argmax(x) for x in gotb]
+    del lg, l32
+    # a short prompt of the same rows, then greedy decode, teacher-forced on the oracle's ids
+    s2 = model.new_sequence(P + DECODE)
+    model.prefill(s2, tokens=prompt[:SAMPLE_ROWS])
+    d32, dbf = [], []
+    for t in gen[:DECODE]:
+        o = model.decode([s2], tokens=to_dev(np.array([t], dtype=np.int32)))
+        d32.append(o["logits32"][0].cpu().numpy())
+        dbf.append(u16(o["logits"])[0])
+    model.check_finite()
+    all64 = np.concatenate([ref64, np.stack(dec64)])
+    allb = np.concatenate([refb, np.stack(decb)])
+    got = np.concatenate([got32, np.stack(d32)])
+    gotbf = np.concatenate([gotb, np.stack(dbf)])
+    err = float(np.abs(got - all64).max())
+    kl = parity.mean_kl(all64, got)
+    counts, detail = parity.judge(parity.bf16_bits_to_f64(allb), parity.bf16_bits_to_f64(gotbf))
+    log(f"config {cfg}: logits max|d| {err:.3e} KL {kl:.2e} judge {counts} {detail}")
+    assert err <= 0.05 and kl <= 1e-3 and parity.top1_gate(counts, all64.shape[0])
+
+    # sampled executions, layer-local per half, in the chunk configuration
+    del model, seq, s2
+    torch.cuda.empty_cache()
+    runner = HalfRunner(g, w, P, P)
+    ins = exec_inputs(g, oracle.embed(W("embed"), ptoks[:SAMPLE_ROWS]), caps, W("final_norm"))
+    empty = np.zeros((1, g.n_kv_heads, g.head_dim), dtype=np.uint16)
+    for e in sampled_execs:
+        b = e % g.n_blocks
+        mid, outr = caps[e]
+        got_mid, _ = runner.run(b, ins[e], empty, empty, 0, "attn", chunk=True)
+        got_out, _ = runner.run(b, mid, empty, empty, 0, "mlp", chunk=True)
+        assert half_report(f"config {cfg} exec {e} attention half", got_mid, mid, ins[e]) >= 0.999
+        assert half_report(f"config {cfg} exec {e} MLP half", got_out, outr, mid) >= 0.999
+
+
+def test_33b_full_model_sampled():
+    _run(3, (0, 25, 51))
+
+
+def test_looped_full_model_sampled():
+    _run(4, (0, 21, 22, 43))

@@ -340,6 +340,18 @@ void ready_flag(llama_model* m, hipStream_t s) {
   }
 }
 
+// Rows enter as token ids (through the embedding) or as hidden rows; a
+// blocks-only model has neither embedding nor logits.
+int check_inputs(const llama_model* m, const void* tok, const void* hin, const void* lb,
+                 const void* l32, const void* next) {
+  if (!tok == !hin) return fail(LLAMA_E_ARG, "give exactly one of token ids and hidden rows");
+  if (!m->d.V) {
+    if (tok) return fail(LLAMA_E_ARG, "a blocks-only model takes hidden rows");
+    if (lb || l32 || next) return fail(LLAMA_E_ARG, "a blocks-only model has no logits");
+  }
+  return LLAMA_OK;
+}
+
 int check_kv(const llama_model* m, const llama_kv* kv) {
   if (!kv) return fail(LLAMA_E_ARG, "cache handle is NULL");
   if (kv->model != m) return fail(LLAMA_E_ARG, "cache belongs to another model");
@@ -467,13 +479,8 @@ int llama_prefill_chunk(llama_model* m, llama_kv* kv, const int32_t* tokens_dev,
   if ((int64_t)pos0 + n_rows > kv->max_positions)
     return fail(LLAMA_E_CAPACITY, "positions %d..%d pass the cache's %d", pos0, pos0 + n_rows - 1,
                 kv->max_positions);
-  if (m->d.V) {
-    if (!tokens_dev || hidden_in_dev) return fail(LLAMA_E_ARG, "a vocabulary model takes tokens");
-  } else {
-    if (tokens_dev || !hidden_in_dev) return fail(LLAMA_E_ARG, "a blocks-only model takes hidden rows");
-    if (logits_bf16_dev || logits_f32_dev || next_token_dev)
-      return fail(LLAMA_E_ARG, "a blocks-only model has no logits");
-  }
+  rc = check_inputs(m, tokens_dev, hidden_in_dev, logits_bf16_dev, logits_f32_dev, next_token_dev);
+  if (rc) return rc;
   rc = check_capture(m, n_rows);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)hip_stream;
@@ -514,15 +521,11 @@ int llama_decode_step(llama_model* m, llama_kv* const* kvs, int32_t n_seq,
       return fail(LLAMA_E_CAPACITY, "sequence %d: positions %d..%d pass the cache's %d", i,
                   kvs[i]->length, kvs[i]->length + rows - 1, kvs[i]->max_positions);
   }
-  if (m->d.V) {
-    if (!tokens_dev || hidden_in_dev) return fail(LLAMA_E_ARG, "a vocabulary model takes tokens");
-  } else {
-    if (tokens_dev || !hidden_in_dev) return fail(LLAMA_E_ARG, "a blocks-only model takes hidden rows");
-    if (logits_bf16_dev || logits_f32_dev || next_tokens_dev)
-      return fail(LLAMA_E_ARG, "a blocks-only model has no logits");
-  }
+  int rc = check_inputs(m, tokens_dev, hidden_in_dev, logits_bf16_dev, logits_f32_dev,
+                        next_tokens_dev);
+  if (rc) return rc;
   const int total = n_seq * rows;
-  int rc = check_capture(m, total);
+  rc = check_capture(m, total);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)hip_stream;
   ready_flag(m, s);

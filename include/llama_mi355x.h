@@ -122,8 +122,9 @@ void* llama_kv_slab(const llama_kv* kv, int32_t exec, int32_t which);
 
 /* One prompt chunk of n_rows (1..max_chunk_rows) rows of one sequence at
  * positions [pos0, pos0 + n_rows); pos0 must equal the cache length.  Rows
- * come from tokens_dev (int32 [n_rows]) through the embedding, or, for a
- * blocks-only model, from hidden_in_dev (bf16 [n_rows][hidden]).  Outputs,
+ * come from exactly one of tokens_dev (int32 [n_rows], through the
+ * embedding) and hidden_in_dev (bf16 [n_rows][hidden], entering the first
+ * execution as they are); a blocks-only model takes hidden rows.  Outputs,
  * each optional (NULL): hidden_out_dev bf16 [n_rows][hidden], the residual
  * after the last execution, before the final norm; logits_bf16_dev and
  * logits_f32_dev ([n_rows or 1][vocab]: every row when all_rows != 0, else
@@ -138,9 +139,9 @@ int llama_prefill_chunk(llama_model* model, llama_kv* kv, const int32_t* tokens_
 
 /* One decode window of `rows` (1..max_window_rows) rows for each of n_seq
  * sequences (1..max_seqs, distinct caches), all batched into one pass: the
- * rows of sequence s sit at positions [len_s, len_s + rows).  tokens_dev is
- * int32 [n_seq][rows] (or hidden_in_dev bf16 [n_seq][rows][hidden] for a
- * blocks-only model); hidden_out_dev, logits_bf16_dev, logits_f32_dev and
+ * rows of sequence s sit at positions [len_s, len_s + rows).  Rows come
+ * from exactly one of tokens_dev (int32 [n_seq][rows]) and hidden_in_dev
+ * (bf16 [n_seq][rows][hidden]); hidden_out_dev, logits_bf16_dev, logits_f32_dev and
  * next_tokens_dev are laid out [n_seq][rows][...], each optional.  Every row
  * is computed exactly as a one-row step at its position would compute it, so
  * windows equal one-row steps and batched sequences equal solo runs bit for

@@ -114,7 +114,8 @@ def test_step_refusals_before_any_launch():
         expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], FAKE, None, 0)
         expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv, kv], FAKE, None, 1)
         expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv, kv2, kv], FAKE, None, 1)
-        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], None, FAKE, 1)  # hidden into a vocab model
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], FAKE, FAKE, 1)  # both inputs
+        expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], None, None, 1)  # neither
         # capacity: the last legal position is usable, the next is refused
         B.llama_kv_set_length(kv, 127)
         expect(B.LLAMA_E_CAPACITY, B.llama_decode_step, m, [kv], FAKE, None, 2)

@@ -76,11 +76,32 @@ def judge_row(ref, test, pos=0):
     return "near-tie"
 
 
+def judge_with_floor(ref_rows, test_rows, floors):
+    """As judge(), but a red row whose two contenders lie within that
+    position's noise floor on the reference side -- how far the reference's
+    own logits move when one input element is nudged by one bf16 step -- is
+    counted as 'drift-tie' instead: at that distance the spec's rounding
+    cannot order the contenders."""
+    counts = {"equal": 0, "near-tie": 0, "drift-tie": 0, "red": 0}
+    detail = []
+    for i, (r, t, f) in enumerate(zip(ref_rows, test_rows, floors)):
+        v = judge_row(r, t, i)
+        if v == "red":
+            a, b = top1(r), top1(t)
+            if abs(float(r[a]) - float(r[b])) <= f:
+                v = "drift-tie"
+        counts[v] += 1
+        if v != "equal":
+            detail.append((i, v))
+    return counts, detail
+
+
 def top1_gate(counts, rows):
     """Teacher-forced top-1 agreement of at least 99%, every miss a near-tie:
     no red row, and at most max(1, 1% of rows) near-ties (on a sample of
     under 100 positions one near-tie is the smallest possible miss)."""
-    return counts["red"] == 0 and counts["near-tie"] <= max(1, int(0.01 * rows))
+    misses = counts["near-tie"] + counts.get("drift-tie", 0)
+    return counts["red"] == 0 and misses <= max(1, int(0.01 * rows))
 
 
 def judge(ref_rows, test_rows):

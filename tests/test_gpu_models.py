@@ -10,8 +10,10 @@ Deep random-init stacks amplify rounding: a one-step change of a single
 embedding element moves the oracle's own 33B logits by up to ~0.4.  So the
 tolerance gates here are layer-local -- sampled executions per half, and the
 head (final norm + lm_head) fed the oracle's final residual through an
-identity block -- while end to end the greedy choices must agree (every miss a
-near-tie) and the logit distance is reported."""
+identity block -- while end to end the greedy choices must agree, every miss a
+near-tie or within the position's noise floor (how far the oracle's own logits
+move when the first row's input is moved by one bf16 step), and the logit
+distance is reported beside that floor."""
 import numpy as np
 import pytest
 
@@ -78,6 +80,21 @@ def _run(cfg, sampled_execs):
         decb.append(rr["logits"][0])
         gen.append(int(rr["tokens"][-1]))
     log(f"config {cfg}: oracle greedy {gen}")
+    # the model's own noise floor: the same rows with every element of the
+    # first row's embedding moved by one bf16 step (a rounding-scale change)
+    class Nudged:
+        def __call__(self, name):
+            a = W(name)
+            if name == "embed":
+                a = a.copy()
+                a[ptoks[0], :] += np.uint16(1)
+            return a
+    om2 = OracleModel(g, Nudged())
+    s2o = om2.new_sequence(SAMPLE_ROWS + DECODE)
+    n64 = [om2.forward(s2o, tokens=ptoks[:SAMPLE_ROWS], logits="all")["logits64"]]
+    for t in gen[:DECODE]:
+        n64.append(om2.forward(s2o, tokens=np.array([t], dtype=np.int32), logits="all")["logits64"])
+    n64 = np.concatenate(n64)
     w = sd.weights(g)
     torch.cuda.synchronize()
 
@@ -127,9 +144,12 @@ def _run(cfg, sampled_execs):
     gotbf = np.concatenate([gotb, np.stack(dbf)])
     err = float(np.abs(got - all64).max())
     kl = parity.mean_kl(all64, got)
-    counts, detail = parity.judge(parity.bf16_bits_to_f64(allb), parity.bf16_bits_to_f64(gotbf))
-    log(f"config {cfg} end to end: logits max|d| {err:.3e} KL {kl:.2e} (reported) judge {counts} "
-        f"{detail}")
+    floors = np.abs(n64 - all64).max(axis=1)
+    counts, detail = parity.judge_with_floor(parity.bf16_bits_to_f64(allb),
+                                             parity.bf16_bits_to_f64(gotbf), floors)
+    log(f"config {cfg} end to end: logits max|d| {err:.3e} KL {kl:.2e} (reported); the oracle "
+        f"nudged by one step moves by up to {floors.max():.3e} (KL "
+        f"{parity.mean_kl(all64, n64):.2e}); judge {counts} {detail}")
     assert parity.top1_gate(counts, all64.shape[0])
 
 

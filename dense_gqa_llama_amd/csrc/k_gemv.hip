@@ -23,6 +23,10 @@ struct GemvArgs {
   int ldo;
   float* out32;
   int ld32;
+  // QKV_ROPE: rows of this launch are rows row0.. of the pass described by tab
+  RowTable tab;
+  const float2* rope;  // [pass rows][d/2] (cos, sin) as bf16 values
+  int nq, nkv, d, row0;
 };
 
 __device__ __forceinline__ float silu_bf16(float g) { return rbf(g / (1.0f + expf(-g))); }
@@ -32,12 +36,29 @@ __device__ __forceinline__ float silu_bf16(float g) { return rbf(g / (1.0f + exp
 template <int R, int NR, int EPI>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
+  static_assert(EPI != GEMV_QKV_ROPE || NR == 4, "rotation pairs come four rows per wave");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * 4 + wave) * COLS;  // first output column of this wave
 
   const u32x4_t* wp[NR];
   int nloc = n0;
-  if (EPI == GEMV_SWIGLU) {
+  int head = 0, i0 = 0;
+  if (EPI == GEMV_QKV_ROPE) {
+    // wave -> head and the rotation pairs (i0, i0 + d/2), (i0 + 1, i0 + 1 + d/2)
+    const int half = a.d >> 1, per_head = half >> 1;
+    const int wv = blockIdx.x * 4 + wave;
+    head = wv / per_head;
+    i0 = 2 * (wv % per_head);
+    const bf16_t* W;
+    int hl;
+    if (head < a.nq) { W = a.seg[0].W; hl = head; }
+    else if (head < a.nq + a.nkv) { W = a.seg[1].W; hl = head - a.nq; }
+    else { W = a.seg[2].W; hl = head - a.nq - a.nkv; }
+    const int base = hl * a.d + i0;
+    const int rows4[4] = {base, base + 1, base + half, base + half + 1};
+#pragma unroll
+    for (int i = 0; i < NR; ++i) wp[i] = (const u32x4_t*)(W + (size_t)rows4[i] * a.K);
+  } else if (EPI == GEMV_SWIGLU) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const bf16_t* W = i < COLS ? a.seg[0].W : a.seg[1].W;
@@ -86,6 +107,37 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[i][r] = wave_sum(acc[i][r]);
 
+  if (EPI == GEMV_QKV_ROPE) {
+    // lane r rotates and stores row r's four outputs
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (lane != r) continue;
+      const int rt = a.row0 + r;
+      const int seq = rt / a.tab.rows_per_seq;
+      const int p = a.tab.pos0[seq] + rt % a.tab.rows_per_seq;
+      const int half = a.d >> 1, kvd = a.nkv * a.d;
+      const float x0 = rbf(acc[0][r]), x1 = rbf(acc[1][r]);
+      const float y0 = rbf(acc[2][r]), y1 = rbf(acc[3][r]);
+      bf16_t* dst;
+      if (head >= a.nq + a.nkv) {  // values: no rotation
+        dst = a.tab.v[seq] + (size_t)p * kvd + (head - a.nq - a.nkv) * a.d + i0;
+        dst[0] = f2bf(x0);
+        dst[1] = f2bf(x1);
+        dst[half] = f2bf(y0);
+        dst[half + 1] = f2bf(y1);
+      } else {
+        dst = head < a.nq ? a.out + (size_t)rt * a.ldo + head * a.d + i0
+                          : a.tab.k[seq] + (size_t)p * kvd + (head - a.nq) * a.d + i0;
+        const float2 c0 = a.rope[(size_t)rt * half + i0], c1 = a.rope[(size_t)rt * half + i0 + 1];
+        dst[0] = f2bf(rbf(x0 * c0.x) + rbf(-y0 * c0.y));
+        dst[half] = f2bf(rbf(y0 * c0.x) + rbf(x0 * c0.y));
+        dst[1] = f2bf(rbf(x1 * c1.x) + rbf(-y1 * c1.y));
+        dst[half + 1] = f2bf(rbf(y1 * c1.x) + rbf(x1 * c1.y));
+      }
+    }
+    return;
+  }
+
   // Spread the stores over lanes: lane (c*R + r) writes column c of row r.
 #pragma unroll
   for (int c = 0; c < COLS; ++c) {
@@ -111,7 +163,8 @@ template <int R, int EPI>
 static void launch_r(const GemvArgs& a, int N, hipStream_t s) {
   // weight rows per wave: more for small windows (more bytes in flight per
   // wave), fewer for large ones (register budget of the R*NR partials).
-  constexpr int NR = EPI == GEMV_SWIGLU ? (R <= 4 ? 4 : 2) : (R <= 2 ? 4 : 2);
+  constexpr int NR = EPI == GEMV_QKV_ROPE ? 4
+                     : EPI == GEMV_SWIGLU ? (R <= 4 ? 4 : 2) : (R <= 2 ? 4 : 2);
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
   int grid = N / (4 * COLS);
   hipLaunchKernelGGL((gemv_kernel<R, NR, EPI>), dim3(grid), dim3(256), 0, s, a);
@@ -143,7 +196,34 @@ void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void
   a.ldo = ldo;
   a.out32 = out32;
   a.ld32 = ld32;
+  a.rope = nullptr;
+  a.nq = a.nkv = a.d = a.row0 = 0;
   if (epi == GEMV_STORE) launch_epi<GEMV_STORE>(rows, a, N, s);
   else if (epi == GEMV_RESIDUAL) launch_epi<GEMV_RESIDUAL>(rows, a, N, s);
   else launch_epi<GEMV_SWIGLU>(rows, a, N, s);
+}
+
+// q/k/v projection of decode rows with RoPE and the cache write fused: q goes
+// to qout [pass rows][nq*d], k and v to their cache slots.
+void launch_gemv_qkv_rope(const GemvSeg* seg, int K, const void* x, int ldx, int rows, int row0,
+                          void* qout, const RowTable& tab, const void* rope, int nq, int nkv,
+                          int d, hipStream_t s) {
+  GemvArgs a;
+  for (int i = 0; i < 3; ++i) a.seg[i] = seg[i];
+  a.nseg = 3;
+  a.K = K;
+  a.x = (const bf16_t*)x;
+  a.ldx = ldx;
+  a.out = (bf16_t*)qout;
+  a.ldo = nq * d;
+  a.out32 = nullptr;
+  a.ld32 = 0;
+  a.tab = tab;
+  a.rope = (const float2*)rope;
+  a.nq = nq;
+  a.nkv = nkv;
+  a.d = d;
+  a.row0 = row0;
+  const int N = (nq + 2 * nkv) * d;  // four columns per wave, 16 per workgroup
+  launch_epi<GEMV_QKV_ROPE>(rows, a, N, s);
 }

@@ -88,46 +88,62 @@ void launch_rmsnorm(const void* h, const void* w, void* out, int rows, int H, fl
 }
 
 // ------------------------------------------------------- RoPE + caching ----
-// Unscaled NeoX RoPE on the q and k heads of each row, then k and v stored at
-// slot p of the row's cache (Nanbeige4.3-33B NInfer card, "Provenance and
-// representation": half-head pairs (i, i + d/2), theta 1.2e8).
+// Unscaled NeoX RoPE (Nanbeige4.3-33B NInfer card, "Provenance and
+// representation": half-head pairs (i, i + d/2), theta 1.2e8):
 //   inv_i = fp32(1 / fp32(theta^(2i/d))), angle a = fp32(p * inv_i),
 //   c, s = bf16(fp32(cos a)), bf16(fp32(sin a)),
 //   x'_i = bf16(bf16(x_i c) + bf16(-x_{i+d/2} s)),
 //   x'_{i+d/2} = bf16(bf16(x_{i+d/2} c) + bf16(x_i s)).
-// cos, sin and the power are evaluated in binary64 and rounded to fp32.
-// One workgroup per row; qkv is the projection output [rows][qd + 2*kvd].
+// The power and cos / sin are evaluated in binary64 and rounded to fp32.
+// Every execution of a pass uses the same positions, so the table of (c, s)
+// per row is computed once per pass.
+__global__ void rope_table_kernel(RowTable tab, int rows, int d, float theta, float2* table) {
+  const int half = d / 2;
+  const int n = rows * half;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < n; t += gridDim.x * blockDim.x) {
+    const int rt = t / half, i = t % half;
+    const int seq = rt / tab.rows_per_seq;
+    const int p = tab.pos0[seq] + rt % tab.rows_per_seq;
+    const float e = (float)(2 * i) / (float)d;
+    const float inv = 1.0f / (float)pow((double)theta, (double)e);
+    const float a = __fmul_rn((float)p, inv);
+    table[t] = make_float2(rbf((float)cos((double)a)), rbf((float)sin((double)a)));
+  }
+}
+
+void launch_rope_table(const RowTable& tab, int rows, int d, float theta, void* table,
+                       hipStream_t s) {
+  int n = rows * (d / 2);
+  int grid = (n + 255) / 256;
+  if (grid > 1024) grid = 1024;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, s, tab, rows, d, theta,
+                     (float2*)table);
+}
+
+// Prompt chunks: RoPE on the q and k heads of each row of the projection
+// output qkv [rows][qd + 2*kvd], then k and v stored at slot p of the row's
+// cache.  One workgroup per row.
 __global__ __launch_bounds__(256) void rope_kv_kernel(const bf16_t* __restrict__ qkv,
                                                       bf16_t* __restrict__ qout, RowTable tab,
-                                                      int nq, int nkv, int d, float theta) {
-  __shared__ float inv[64];
-  __shared__ float cs[64], sn[64];
-  int rt = blockIdx.x;
-  int seq = rt / tab.rows_per_seq;
-  int p = tab.pos0[seq] + rt % tab.rows_per_seq;
-  int half = d / 2;
-  if (threadIdx.x < half) {
-    int i = threadIdx.x;
-    float e = (float)(2 * i) / (float)d;
-    float pw = (float)pow((double)theta, (double)e);
-    inv[i] = 1.0f / pw;
-    float a = __fmul_rn((float)p, inv[i]);
-    cs[i] = rbf((float)cos((double)a));
-    sn[i] = rbf((float)sin((double)a));
-  }
-  __syncthreads();
-  int qd = nq * d, kvd = nkv * d;
+                                                      int nq, int nkv, int d,
+                                                      const float2* __restrict__ table) {
+  const int rt = blockIdx.x;
+  const int seq = rt / tab.rows_per_seq;
+  const int p = tab.pos0[seq] + rt % tab.rows_per_seq;
+  const int half = d / 2;
+  const int qd = nq * d, kvd = nkv * d;
   const bf16_t* src = qkv + (size_t)rt * (qd + 2 * kvd);
   bf16_t* kdst = tab.k[seq] + (size_t)p * kvd;
   bf16_t* vdst = tab.v[seq] + (size_t)p * kvd;
-  int items = (nq + nkv) * half;
+  const float2* cs = table + (size_t)rt * half;
+  const int items = (nq + nkv) * half;
   for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    int hh = it / half, i = it % half;
+    const int hh = it / half, i = it % half;
     const bf16_t* x = src + hh * d;  // q heads then k heads, contiguous
-    float x1 = bf2f(x[i]), x2 = bf2f(x[i + half]);
-    float c = cs[i], s = sn[i];
-    bf16_t o1 = f2bf(rbf(x1 * c) + rbf(-x2 * s));
-    bf16_t o2 = f2bf(rbf(x2 * c) + rbf(x1 * s));
+    const float x1 = bf2f(x[i]), x2 = bf2f(x[i + half]);
+    const float2 c = cs[i];
+    const bf16_t o1 = f2bf(rbf(x1 * c.x) + rbf(-x2 * c.y));
+    const bf16_t o2 = f2bf(rbf(x2 * c.x) + rbf(x1 * c.y));
     bf16_t* dst = hh < nq ? qout + (size_t)rt * qd + hh * d : kdst + (hh - nq) * d;
     dst[i] = o1;
     dst[i + half] = o2;
@@ -138,31 +154,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const bf16_t* __restrict__
 }
 
 void launch_rope_kv(const void* qkv, void* qout, const RowTable& tab, int rows, int nq, int nkv,
-                    int d, float theta, hipStream_t s) {
+                    int d, const void* table, hipStream_t s) {
   hipLaunchKernelGGL(rope_kv_kernel, dim3(rows), dim3(256), 0, s, (const bf16_t*)qkv,
-                     (bf16_t*)qout, tab, nq, nkv, d, theta);
-}
-
-// --------------------------------------------------------------- SwiGLU ----
-// m = bf16(bf16(silu(g)) * u) over gu = [rows][2F] (gate then up halves).
-__global__ __launch_bounds__(256) void swiglu_kernel(const bf16_t* __restrict__ gu,
-                                                     bf16_t* __restrict__ m, int F, int rows) {
-  size_t n = (size_t)rows * F;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    size_t r = i / F, j = i % F;
-    float g = bf2f(gu[r * 2 * F + j]), u = bf2f(gu[r * 2 * F + F + j]);
-    float sg = rbf(g / (1.0f + expf(-g)));
-    m[i] = f2bf(sg * u);
-  }
-}
-
-void launch_swiglu(const void* gu, void* m, int F, int rows, hipStream_t s) {
-  size_t n = (size_t)rows * F;
-  int grid = (int)((n + 255) / 256);
-  if (grid > 4096) grid = 4096;
-  hipLaunchKernelGGL(swiglu_kernel, dim3(grid), dim3(256), 0, s, (const bf16_t*)gu, (bf16_t*)m,
-                     F, rows);
+                     (bf16_t*)qout, tab, nq, nkv, d, (const float2*)table);
 }
 
 // --------------------------------------------------------------- argmax ----

@@ -21,16 +21,19 @@ void launch_embed(const void* E, int vocab, int H, const int32_t* tok, void* h, 
                   hipStream_t s);
 void launch_rmsnorm(const void* h, const void* w, void* out, int rows, int H, float eps,
                     hipStream_t s);
+// (cos, sin) of every row's position, [rows][d/2] float2 of bf16 values,
+// computed once per pass and read by every execution.
+void launch_rope_table(const RowTable& tab, int rows, int d, float theta, void* table,
+                       hipStream_t s);
 void launch_rope_kv(const void* qkv, void* qout, const RowTable& tab, int rows, int nq, int nkv,
-                    int d, float theta, hipStream_t s);
-void launch_swiglu(const void* gu, void* m, int F, int rows, hipStream_t s);
+                    int d, const void* table, hipStream_t s);
 int argmax_chunks(int V);
 void launch_argmax(const void* logits, int V, int ld, int rows, float* pv, int* pi, int32_t* out,
                    int* flag, hipStream_t s);
 
 // Decode projections (1..16 rows).  Output columns [0, N) are the
 // concatenation of up to three weight matrices (segments), each [rows][K].
-enum GemvEpilogue { GEMV_STORE = 0, GEMV_RESIDUAL = 1, GEMV_SWIGLU = 2 };
+enum GemvEpilogue { GEMV_STORE = 0, GEMV_RESIDUAL = 1, GEMV_SWIGLU = 2, GEMV_QKV_ROPE = 3 };
 struct GemvSeg {
   const uint16_t* W;
   int n_begin, n_end;
@@ -41,6 +44,11 @@ struct GemvSeg {
 //           out[r*ldo + n] = bf16(bf16(silu(bf16(g))) * bf16(u)).
 void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* x, int ldx,
                  int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s);
+// q/k/v decode projection with RoPE and the cache write fused (seg = q, k, v
+// weights); rows are rows row0.. of the pass tab describes; q goes to qout.
+void launch_gemv_qkv_rope(const GemvSeg* seg, int K, const void* x, int ldx, int rows, int row0,
+                          void* qout, const RowTable& tab, const void* rope, int nq, int nkv,
+                          int d, hipStream_t s);
 
 // Prompt-chunk projections on the matrix cores; ncols tile columns (N, or
 // 2F for SWIGLU, whose tiles interleave 32 gate and 32 up rows).
@@ -52,8 +60,8 @@ void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* s
 void launch_attn_prefill(const void* q, const void* kc, const void* vc, int rows, int pos0, int nq,
                          int nkv, int d, void* out, hipStream_t s);
 
-// Decode attention: split over key blocks at absolute positions, then a
-// merge in block order.
-int attn_key_block();
+// Decode attention: split over key blocks at absolute positions, then
+// merged in block order.
+int attn_max_blocks();
 void launch_attn_decode(const void* q, const RowTable& tab, int rows, int nq, int nkv, int d,
-                        float* part, int max_blocks, void* out, hipStream_t s);
+                        float* part, void* out, hipStream_t s);

@@ -32,7 +32,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Device workspace carved into fixed regions.
 struct Layout {
-  size_t h, x, qkv, q, att, m, logits, amx_v, amx_i, part, flag, total;
+  size_t h, x, qkv, q, att, m, rope, logits, amx_v, amx_i, part, flag, total;
 };
 
 struct Dims {
@@ -40,7 +40,6 @@ struct Dims {
   int M;      // largest number of rows one pass carries
   int Mdec;   // rows of one decode step (seqs * window)
   int Llog;   // rows of the internal logits buffer
-  int max_blocks;
 };
 
 Dims dims_of(const llama_config& c, int max_positions) {
@@ -57,7 +56,7 @@ Dims dims_of(const llama_config& c, int max_positions) {
   d.Mdec = c.max_seqs * c.max_window_rows;
   d.M = std::max(d.Mdec, c.max_chunk_rows);
   d.Llog = std::max(d.Mdec, 16);
-  d.max_blocks = (max_positions + attn_key_block() - 1) / attn_key_block();
+  (void)max_positions;  // decode attention keeps at most attn_max_blocks() partials per row
   return d;
 }
 
@@ -75,11 +74,12 @@ Layout layout_of(const Dims& d) {
   L.q = take((size_t)d.M * d.qd * 2);
   L.att = take((size_t)d.M * d.qd * 2);
   L.m = take((size_t)d.M * d.F * 2);
+  L.rope = take((size_t)d.M * (d.d / 2) * 8);
   int nch = d.V ? argmax_chunks(d.V) : 1;
   L.logits = take((size_t)d.Llog * std::max(d.V, 1) * 2);
   L.amx_v = take((size_t)d.Llog * nch * 4);
   L.amx_i = take((size_t)d.Llog * nch * 4);
-  L.part = take((size_t)d.Mdec * d.nq * d.max_blocks * (d.d + 2) * 4);
+  L.part = take((size_t)d.Mdec * d.nq * attn_max_blocks() * (d.d + 2) * 4);
   L.flag = take(256);
   L.total = off;
   return L;
@@ -224,10 +224,12 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
   uint16_t* att = m->at<uint16_t>(m->L.att);
   uint16_t* mm = m->at<uint16_t>(m->L.m);
   float* part = m->at<float>(m->L.part);
+  void* rope = m->ws + m->L.rope;
   const size_t rowb = (size_t)d.H * 2;
 
   if (tok) launch_embed(m->embed, d.V, d.H, tok, h, rows, p.s);
   else (void)hipMemcpyAsync(h, hin, rows * rowb, hipMemcpyDeviceToDevice, p.s);
+  launch_rope_table(table_for(p, 0), rows, d.d, (float)c.rope_theta, rope, p.s);
 
   for (int loop = 0; loop < c.n_loops; ++loop) {
     for (int b = 0; b < c.n_blocks; ++b) {
@@ -247,7 +249,7 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
           launch_gemm(GEMV_STORE, x, d.H, rows, d.H, qkvseg, 3, nullptr, nullptr, qkv, nqkv,
                       nullptr, 0, nqkv, p.s);
         }
-        launch_rope_kv(qkv, q, tab, rows, d.nq, d.nkv, d.d, (float)c.rope_theta, p.s);
+        launch_rope_kv(qkv, q, tab, rows, d.nq, d.nkv, d.d, rope, p.s);
         {
           Timed t(m, LLAMA_TIMING_PREFILL_ATTN, p.s);
           launch_attn_prefill(q, tab.k[0], tab.v[0], rows, p.pos0[0], d.nq, d.nkv, d.d, att, p.s);
@@ -260,12 +262,13 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
       } else {
         {
           Timed t(m, LLAMA_TIMING_QKV, p.s);
-          gemv_rows(GEMV_STORE, qkvseg, 3, nqkv, d.H, x, d.H, rows, qkv, nqkv, nullptr, 0, p.s);
+          for (int r0 = 0; r0 < rows; r0 += 16)
+            launch_gemv_qkv_rope(qkvseg, d.H, x + (size_t)r0 * d.H, d.H, std::min(16, rows - r0),
+                                 r0, q, tab, rope, d.nq, d.nkv, d.d, p.s);
         }
-        launch_rope_kv(qkv, q, tab, rows, d.nq, d.nkv, d.d, (float)c.rope_theta, p.s);
         {
           Timed t(m, LLAMA_TIMING_ATTN, p.s);
-          launch_attn_decode(q, tab, rows, d.nq, d.nkv, d.d, part, d.max_blocks, att, p.s);
+          launch_attn_decode(q, tab, rows, d.nq, d.nkv, d.d, part, att, p.s);
         }
         {
           Timed t(m, LLAMA_TIMING_O, p.s);

@@ -52,3 +52,50 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// RMSNorm, bf16(w * bf16(x * r)) with r = 1/sqrt(sum(x^2)/H + eps) (pull
+// request "llama: Nanbeige4.3-33B on Metal, the bf16 release served as
+// published", section "How").  One canonical order for the sum, used by the
+// standalone norm kernel and by every projection that normalises its input
+// rows itself, so a row's bits never depend on which of the two ran: a full
+// wave sums the row, lane l taking 16-byte vectors l, l+64, ... in order with
+// fused multiply-adds, then the xor butterfly.  H is a multiple of 8.
+__device__ __forceinline__ float row_inv_rms(const bf16_t* __restrict__ x, int H, float eps) {
+  const u32x4_t* xv = (const u32x4_t*)x;
+  const int nv = H / 8;
+  float ss = 0.f;
+  // loads are issued eight at a time; the sum still runs in vector order
+  for (int v0 = lane_id(); v0 < nv; v0 += 8 * WAVE) {
+    u32x4_t q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int v = v0 + i * WAVE;
+      q[i] = v < nv ? xv[v] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (v0 + i * WAVE >= nv) break;
+      const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = bf_lo(w[j]), b = bf_hi(w[j]);
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  return 1.0f / sqrtf(ss / (float)H + eps);
+}
+
+// Eight normalised elements: bf16(w * bf16(x * r)), packed.
+__device__ __forceinline__ u32x4_t norm8(u32x4_t x, u32x4_t w, float r) {
+  const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float n0 = rbf(bf_lo(xs[j]) * r), n1 = rbf(bf_hi(xs[j]) * r);
+    o[j] = pack_bf2(f2bf(bf_lo(ws[j]) * n0), f2bf(bf_hi(ws[j]) * n1));
+  }
+  return u32x4_t{o[0], o[1], o[2], o[3]};
+}

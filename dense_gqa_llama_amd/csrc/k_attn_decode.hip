@@ -125,12 +125,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
       o0[h] *= As[h];
       o1[h] *= As[h];
     }
-    for (int k = grp; k < nk; k += NG) {
-      uint32_t vv = vbase[(size_t)(s0 + k) * (kvd / 2)];
-      float v0 = bf_lo(vv), v1 = bf_hi(vv);
+    // all of this lane's value loads are issued before any is used
+    constexpr int KPL = SUB / NG;  // slots per lane
+    uint32_t vv[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int k = grp + i * NG;
+      vv[i] = k < nk ? vbase[(size_t)(s0 + k) * (kvd / 2)] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int k = grp + i * NG;
+      if (k >= nk) break;
+      const float v0 = bf_lo(vv[i]), v1 = bf_hi(vv[i]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float e = S[h][k];
+        const float e = S[h][k];
         o0[h] = fmaf(e, v0, o0[h]);
         o1[h] = fmaf(e, v1, o1[h]);
       }

@@ -27,14 +27,18 @@ struct GemvArgs {
   RowTable tab;
   const float2* rope;  // [pass rows][d/2] (cos, sin) as bf16 values
   int nq, nkv, d, row0;
+  // NORM: the input rows are raw residuals, normalised here with this weight
+  const bf16_t* normw;
+  float eps;
 };
 
 __device__ __forceinline__ float silu_bf16(float g) { return rbf(g / (1.0f + expf(-g))); }
 
 // NR weight rows per wave; for SWIGLU the first NR/2 come from the gate
 // matrix and the last NR/2 from the up matrix, for the same output columns.
-template <int R, int NR, int EPI>
+template <int R, int NR, int EPI, bool NORM, bool XLDS>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+  extern __shared__ u32x4_t sx[];  // XLDS: the (normalised) input rows, [R][K/8]
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
   static_assert(EPI != GEMV_QKV_ROPE || NR == 4, "rotation pairs come four rows per wave");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -83,14 +87,48 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int nv = a.K >> 3;
   const u32x4_t* xb = (const u32x4_t*)a.x;
   const int xs = a.ldx >> 3;
-#pragma unroll 2
+  // Software pipeline: the weight vectors of the next step are in flight
+  // while this step's are consumed; the first step's loads are issued before
+  // the norm prologue so its row reads overlap them.
+  u32x4_t wn[NR];
+  if (lane < nv) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) wn[i] = __builtin_nontemporal_load(wp[i] + lane);
+  }
+  float rs[R];
+  if (NORM) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) rs[r] = row_inv_rms(a.x + (size_t)r * a.ldx, a.K, a.eps);
+  }
+  const u32x4_t* nw = (const u32x4_t*)a.normw;
+  if (XLDS) {
+    for (int i = threadIdx.x; i < R * nv; i += blockDim.x) {
+      const int r = i / nv, v = i - r * nv;
+      u32x4_t xv = xb[r * xs + v];
+      if (NORM) xv = norm8(xv, nw[v], rs[r]);
+      sx[i] = xv;
+    }
+    __syncthreads();
+  }
   for (int v = lane; v < nv; v += WAVE) {
     u32x4_t w[NR];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) w[i] = __builtin_nontemporal_load(wp[i] + v);
+    for (int i = 0; i < NR; ++i) w[i] = wn[i];
+    if (v + WAVE < nv) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) wn[i] = __builtin_nontemporal_load(wp[i] + v + WAVE);
+    }
+    u32x4_t g;
+    if (NORM && !XLDS) g = nw[v];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      u32x4_t xv = xb[r * xs + v];
+      u32x4_t xv;
+      if (XLDS) {
+        xv = sx[r * nv + v];
+      } else {
+        xv = xb[r * xs + v];
+        if (NORM) xv = norm8(xv, g, rs[r]);
+      }
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         float t = acc[i][r];
@@ -159,7 +197,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
 }
 
-template <int R, int EPI>
+// Input rows are staged in LDS when they fit in this many bytes.
+constexpr int GEMV_XLDS_BYTES = 64 * 1024;
+
+template <int R, int EPI, bool NORM>
 static void launch_r(const GemvArgs& a, int N, hipStream_t s) {
   // weight rows per wave: more for small windows (more bytes in flight per
   // wave), fewer for large ones (register budget of the R*NR partials).
@@ -167,14 +208,31 @@ static void launch_r(const GemvArgs& a, int N, hipStream_t s) {
                      : EPI == GEMV_SWIGLU ? (R <= 4 ? 4 : 2) : (R <= 2 ? 4 : 2);
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
   int grid = N / (4 * COLS);
-  hipLaunchKernelGGL((gemv_kernel<R, NR, EPI>), dim3(grid), dim3(256), 0, s, a);
+  const size_t xbytes = (size_t)R * a.K * 2;
+  if (xbytes <= GEMV_XLDS_BYTES)
+    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, true>), dim3(grid), dim3(256), xbytes, s, a);
+  else
+    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, false>), dim3(grid), dim3(256), 0, s, a);
 }
 
+// Inputs are normalised inside the projection for windows of up to
+// GEMV_NORM_ROWS rows; larger windows arrive normalised by rmsnorm_kernel
+// (same bits, one canonical order).
 template <int EPI>
 static void launch_epi(int rows, const GemvArgs& a, int N, hipStream_t s) {
+  if (a.normw) {
+    switch (rows) {
+      case 1: launch_r<1, EPI, true>(a, N, s); break;
+      case 2: launch_r<2, EPI, true>(a, N, s); break;
+      case 3: launch_r<3, EPI, true>(a, N, s); break;
+      case 4: launch_r<4, EPI, true>(a, N, s); break;
+      default: break;
+    }
+    return;
+  }
   switch (rows) {
 #define CASE(R) \
-  case R: launch_r<R, EPI>(a, N, s); break;
+  case R: launch_r<R, EPI, false>(a, N, s); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
     CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
 #undef CASE
@@ -185,7 +243,8 @@ static void launch_epi(int rows, const GemvArgs& a, int N, hipStream_t s) {
 // Column counts must be multiples of 16 (every served width is a multiple of
 // 128), so no wave straddles a segment or the end.
 void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* x, int ldx,
-                 int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s) {
+                 int rows, void* out, int ldo, float* out32, int ld32, const void* normw,
+                 float eps, hipStream_t s) {
   GemvArgs a;
   for (int i = 0; i < 3; ++i) a.seg[i] = i < nseg ? seg[i] : seg[0];
   a.nseg = nseg;
@@ -198,6 +257,8 @@ void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void
   a.ld32 = ld32;
   a.rope = nullptr;
   a.nq = a.nkv = a.d = a.row0 = 0;
+  a.normw = rows <= GEMV_NORM_ROWS ? (const bf16_t*)normw : nullptr;
+  a.eps = eps;
   if (epi == GEMV_STORE) launch_epi<GEMV_STORE>(rows, a, N, s);
   else if (epi == GEMV_RESIDUAL) launch_epi<GEMV_RESIDUAL>(rows, a, N, s);
   else launch_epi<GEMV_SWIGLU>(rows, a, N, s);
@@ -207,7 +268,7 @@ void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void
 // to qout [pass rows][nq*d], k and v to their cache slots.
 void launch_gemv_qkv_rope(const GemvSeg* seg, int K, const void* x, int ldx, int rows, int row0,
                           void* qout, const RowTable& tab, const void* rope, int nq, int nkv,
-                          int d, hipStream_t s) {
+                          int d, const void* normw, float eps, hipStream_t s) {
   GemvArgs a;
   for (int i = 0; i < 3; ++i) a.seg[i] = seg[i];
   a.nseg = 3;
@@ -224,6 +285,8 @@ void launch_gemv_qkv_rope(const GemvSeg* seg, int K, const void* x, int ldx, int
   a.nkv = nkv;
   a.d = d;
   a.row0 = row0;
+  a.normw = rows <= GEMV_NORM_ROWS ? (const bf16_t*)normw : nullptr;
+  a.eps = eps;
   const int N = (nq + 2 * nkv) * d;  // four columns per wave, 16 per workgroup
   launch_epi<GEMV_QKV_ROPE>(rows, a, N, s);
 }

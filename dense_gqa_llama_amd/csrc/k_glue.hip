@@ -39,52 +39,25 @@ void launch_embed(const void* E, int vocab, int H, const int32_t* tok, void* h, 
 }
 
 // -------------------------------------------------------------- RMSNorm ----
-// out = bf16(w * bf16(x * r)), r = 1/sqrt(sum(x^2)/H + eps).  One 256-thread
-// workgroup per row; each thread sums its 8-element slices in order, then the
-// four waves' sums are added in wave order, so every row (whatever the batch)
-// sees the same association.  In place (out == h) is allowed: after the
-// barrier that completes the sum, each element is read and then written by
-// one thread only.
+// out = bf16(w * bf16(x * r)) in the canonical order of row_inv_rms: one wave
+// per row, four rows per workgroup.  In place (out == h) is allowed: each
+// element is read and then written by the same lane, after the row's sum.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const bf16_t* h, const bf16_t* __restrict__ w,
-                                                      bf16_t* out, int H, float eps) {
-  __shared__ float part[4];
-  int r = blockIdx.x;
-  const uint4* x = (const uint4*)(h + (size_t)r * H);
-  int nv = H / 8;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < nv; i += 256) {
-    uint4 v = x[i];
-    uint32_t q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float a = bf_lo(q[j]), b = bf_hi(q[j]);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-    }
-  }
-  ss = wave_sum(ss);
-  if (lane_id() == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = ((part[0] + part[1]) + part[2]) + part[3];
-  float rs = 1.0f / sqrtf(tot / (float)H + eps);
-  const uint4* wv = (const uint4*)w;
-  uint4* o = (uint4*)(out + (size_t)r * H);
-  for (int i = threadIdx.x; i < nv; i += 256) {
-    uint4 v = x[i], g = wv[i];
-    uint32_t q[4] = {v.x, v.y, v.z, v.w}, ww[4] = {g.x, g.y, g.z, g.w}, res[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float n0 = rbf(bf_lo(q[j]) * rs), n1 = rbf(bf_hi(q[j]) * rs);
-      res[j] = pack_bf2(f2bf(bf_lo(ww[j]) * n0), f2bf(bf_hi(ww[j]) * n1));
-    }
-    o[i] = make_uint4(res[0], res[1], res[2], res[3]);
-  }
+                                                      bf16_t* out, int rows, int H, float eps) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // uniform per wave; no barrier follows
+  const bf16_t* x = h + (size_t)r * H;
+  const float rs = row_inv_rms(x, H, eps);
+  const u32x4_t* xv = (const u32x4_t*)x;
+  const u32x4_t* wv = (const u32x4_t*)w;
+  u32x4_t* o = (u32x4_t*)(out + (size_t)r * H);
+  for (int v = lane_id(); v < H / 8; v += WAVE) o[v] = norm8(xv[v], wv[v], rs);
 }
 
 void launch_rmsnorm(const void* h, const void* w, void* out, int rows, int H, float eps,
                     hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, (const bf16_t*)h,
-                     (const bf16_t*)w, (bf16_t*)out, H, eps);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, (const bf16_t*)h,
+                     (const bf16_t*)w, (bf16_t*)out, rows, H, eps);
 }
 
 // ------------------------------------------------------- RoPE + caching ----

@@ -42,13 +42,18 @@ struct GemvSeg {
 // RESIDUAL: out[r*ldo + n] = bf16(out + bf16(acc))  (the residual stream).
 // SWIGLU:   seg[0] = gate, seg[1] = up, both with n in [0, F):
 //           out[r*ldo + n] = bf16(bf16(silu(bf16(g))) * bf16(u)).
+// normw (nullable): the input rows are raw residuals to be normalised with
+// this RMSNorm weight -- done inside the projection when rows <=
+// GEMV_NORM_ROWS; callers normalise larger windows first and pass NULL.
+#define GEMV_NORM_ROWS 4
 void launch_gemv(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* x, int ldx,
-                 int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s);
+                 int rows, void* out, int ldo, float* out32, int ld32, const void* normw,
+                 float eps, hipStream_t s);
 // q/k/v decode projection with RoPE and the cache write fused (seg = q, k, v
 // weights); rows are rows row0.. of the pass tab describes; q goes to qout.
 void launch_gemv_qkv_rope(const GemvSeg* seg, int K, const void* x, int ldx, int rows, int row0,
                           void* qout, const RowTable& tab, const void* rope, int nq, int nkv,
-                          int d, hipStream_t s);
+                          int d, const void* normw, float eps, hipStream_t s);
 
 // Prompt-chunk projections on the matrix cores; ncols tile columns (N, or
 // 2F for SWIGLU, whose tiles interleave 32 gate and 32 up rows).

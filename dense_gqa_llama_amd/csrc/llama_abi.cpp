@@ -198,19 +198,25 @@ struct Timed {
 
 // Projection over all rows in launches of at most 16 rows.
 void gemv_rows(int epi, const GemvSeg* seg, int nseg, int N, int K, const void* x, int ldx,
-               int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s) {
+               int rows, void* out, int ldo, float* out32, int ld32, hipStream_t s,
+               const void* normw = nullptr, float eps = 0.f) {
   for (int r0 = 0; r0 < rows; r0 += 16) {
     int n = std::min(16, rows - r0);
     launch_gemv(epi, seg, nseg, N, K, (const uint16_t*)x + (size_t)r0 * ldx, ldx, n,
                 (uint16_t*)out + (size_t)r0 * ldo, ldo, out32 ? out32 + (size_t)r0 * ld32 : nullptr,
-                ld32, s);
+                ld32, normw, eps, s);
   }
 }
 
+// Decode windows of up to GEMV_NORM_ROWS rows normalise inside the
+// projections (q/k/v, gate/up, lm_head) instead of running rmsnorm_kernel;
+// both use one canonical order, so the bits are the same either way.
+bool norm_fused(bool chunk, int rows) { return !chunk && rows <= GEMV_NORM_ROWS; }
+
 // Runs the block stack over the pass's rows.  On return ws.h holds the
-// residual after the last execution and, when the model has a vocabulary,
-// ws.x the final-normed rows.  cap_row0 / cap_rows place these rows in the
-// capture buffer.
+// residual after the last execution and, when the model has a vocabulary and
+// the norm is not fused, ws.x the final-normed rows.  cap_row0 / cap_rows
+// place these rows in the capture buffer.
 void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, int cap_row0,
                int cap_rows, bool chunk) {
   llama_model* m = p.m;
@@ -226,6 +232,7 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
   float* part = m->at<float>(m->L.part);
   void* rope = m->ws + m->L.rope;
   const size_t rowb = (size_t)d.H * 2;
+  const bool fuse = norm_fused(chunk, rows);
 
   if (tok) launch_embed(m->embed, d.V, d.H, tok, h, rows, p.s);
   else (void)hipMemcpyAsync(h, hin, rows * rowb, hipMemcpyDeviceToDevice, p.s);
@@ -237,7 +244,7 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
       const llama_block_weights& w = m->blocks[b];
       RowTable tab = table_for(p, e);
 
-      launch_rmsnorm(h, w.attn_norm, x, rows, d.H, c.rms_eps, p.s);
+      if (!fuse) launch_rmsnorm(h, w.attn_norm, x, rows, d.H, c.rms_eps, p.s);
       GemvSeg qkvseg[3] = {{(const uint16_t*)w.q, 0, d.qd},
                            {(const uint16_t*)w.k, d.qd, d.qd + d.kvd},
                            {(const uint16_t*)w.v, d.qd + d.kvd, d.qd + 2 * d.kvd}};
@@ -262,9 +269,11 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
       } else {
         {
           Timed t(m, LLAMA_TIMING_QKV, p.s);
+          const uint16_t* in = fuse ? h : x;
           for (int r0 = 0; r0 < rows; r0 += 16)
-            launch_gemv_qkv_rope(qkvseg, d.H, x + (size_t)r0 * d.H, d.H, std::min(16, rows - r0),
-                                 r0, q, tab, rope, d.nq, d.nkv, d.d, p.s);
+            launch_gemv_qkv_rope(qkvseg, d.H, in + (size_t)r0 * d.H, d.H, std::min(16, rows - r0),
+                                 r0, q, tab, rope, d.nq, d.nkv, d.d, fuse ? w.attn_norm : nullptr,
+                                 c.rms_eps, p.s);
         }
         {
           Timed t(m, LLAMA_TIMING_ATTN, p.s);
@@ -279,7 +288,7 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
         (void)hipMemcpy2DAsync((uint8_t*)m->cap + (((size_t)e * 2 + 0) * cap_rows + cap_row0) * rowb,
                          rowb, h, rowb, rowb, rows, hipMemcpyDeviceToDevice, p.s);
 
-      launch_rmsnorm(h, w.mlp_norm, x, rows, d.H, c.rms_eps, p.s);
+      if (!fuse) launch_rmsnorm(h, w.mlp_norm, x, rows, d.H, c.rms_eps, p.s);
       GemvSeg gu[2] = {{(const uint16_t*)w.gate, 0, d.F}, {(const uint16_t*)w.up, 0, d.F}};
       GemvSeg dseg[1] = {{(const uint16_t*)w.down, 0, d.H}};
       if (chunk) {
@@ -291,7 +300,8 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
       } else {
         {
           Timed t(m, LLAMA_TIMING_GATE_UP, p.s);
-          gemv_rows(GEMV_SWIGLU, gu, 2, d.F, d.H, x, d.H, rows, mm, d.F, nullptr, 0, p.s);
+          gemv_rows(GEMV_SWIGLU, gu, 2, d.F, d.H, fuse ? h : x, d.H, rows, mm, d.F, nullptr, 0,
+                    p.s, fuse ? w.mlp_norm : nullptr, c.rms_eps);
         }
         {
           Timed t(m, LLAMA_TIMING_DOWN, p.s);
@@ -304,16 +314,18 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
     }
     const bool last = loop == c.n_loops - 1;
     if (last && hout) (void)hipMemcpyAsync(hout, h, rows * rowb, hipMemcpyDeviceToDevice, p.s);
-    if (d.V) {
-      // final norm at the end of every loop; it replaces the residual between loops
+    if (d.V && !(last && fuse)) {
+      // final norm at the end of every loop; it replaces the residual between
+      // loops (after the last, a fused head normalises its rows itself)
       launch_rmsnorm(h, m->final_norm, last ? x : h, rows, d.H, c.rms_eps, p.s);
     }
   }
 }
 
-// lm_head over `rows` final-normed rows starting at x, then the greedy draw.
+// lm_head over `rows` rows starting at x, then the greedy draw.  The rows
+// are final-normed, or with normw raw residuals the projection normalises.
 void run_head(llama_model* m, const uint16_t* x, int rows, void* logits_bf16, float* logits_f32,
-              int32_t* next, hipStream_t s) {
+              int32_t* next, hipStream_t s, const void* normw = nullptr) {
   const Dims& d = m->d;
   GemvSeg seg[1] = {{(const uint16_t*)m->lm_head, 0, d.V}};
   for (int r0 = 0; r0 < rows; r0 += d.Llog) {
@@ -323,7 +335,8 @@ void run_head(llama_model* m, const uint16_t* x, int rows, void* logits_bf16, fl
     {
       Timed t(m, LLAMA_TIMING_LM_HEAD, s);
       gemv_rows(GEMV_STORE, seg, 1, d.V, d.H, x + (size_t)r0 * d.H, d.H, n, lb, d.V,
-                logits_f32 ? logits_f32 + (size_t)r0 * d.V : nullptr, d.V, s);
+                logits_f32 ? logits_f32 + (size_t)r0 * d.V : nullptr, d.V, s, normw,
+                m->cfg.rms_eps);
     }
     if (next)
       launch_argmax(lb, d.V, d.V, n, m->at<float>(m->L.amx_v), m->at<int>(m->L.amx_i), next + r0,
@@ -535,9 +548,11 @@ int llama_decode_step(llama_model* m, llama_kv* const* kvs, int32_t n_seq,
   Pass p{m, kvs, n_seq, rows, {0}, s};
   for (int i = 0; i < n_seq; ++i) p.pos0[i] = kvs[i]->length;
   run_stack(p, tokens_dev, hidden_in_dev, hidden_out_dev, 0, total, false);
-  if (m->d.V && (logits_bf16_dev || logits_f32_dev || next_tokens_dev))
-    run_head(m, m->at<uint16_t>(m->L.x), total, logits_bf16_dev, logits_f32_dev, next_tokens_dev,
-             s);
+  if (m->d.V && (logits_bf16_dev || logits_f32_dev || next_tokens_dev)) {
+    const bool fuse = norm_fused(false, total);
+    run_head(m, m->at<uint16_t>(fuse ? m->L.h : m->L.x), total, logits_bf16_dev, logits_f32_dev,
+             next_tokens_dev, s, fuse ? m->final_norm : nullptr);
+  }
   rc = dev_check("decode launch");
   if (rc) return rc;
   for (int i = 0; i < n_seq; ++i) kvs[i]->length += rows;

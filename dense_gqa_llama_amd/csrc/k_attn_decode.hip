@@ -55,32 +55,53 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kvd = nkv * D;
 
+  const int dp = tid % DP, grp = tid / DP;
+  const float scale = 1.0f / sqrtf((float)D);
+  const bf16_t* kbase = tab.k[seq] + (size_t)g * D;
+  const uint32_t* vbase = (const uint32_t*)(tab.v[seq] + (size_t)g * D) + dp;
+  const int kslot = tid >> 2, qq = tid & 3;  // score pass: lanes 4k..4k+3 share slot k
+  constexpr int KPL = SUB / NG;              // value pass: slots per lane
+
+  // The key and value loads of a sub-block are issued together, one
+  // sub-block ahead of their use, so a block costs one memory round trip
+  // rather than three (query, keys, then values).
+  u32x4_t kreg[DQ / 8];
+  uint32_t vv[KPL];
+  auto issue = [&](int s0) {
+    const int nk = min(SUB, end - s0);
+    if (kslot < nk) {
+      const u32x4_t* krow = (const u32x4_t*)(kbase + (size_t)(s0 + kslot) * kvd + qq * DQ);
+#pragma unroll
+      for (int j = 0; j < DQ / 8; ++j) kreg[j] = krow[j];
+    }
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int k = grp + i * NG;
+      vv[i] = k < nk ? vbase[(size_t)(s0 + k) * (kvd / 2)] : 0u;
+    }
+  };
+  issue(start);
+
   const uint32_t* qsrc = (const uint32_t*)(q + ((size_t)rt * nq + (size_t)g * G) * D);
   for (int i = tid; i < G * DP; i += 256) qs[i / DP][i % DP] = qsrc[i];
   if (tid < G) { Ms[tid] = -INFINITY; Ls[tid] = 0.f; }
 
-  const int dp = tid % DP, grp = tid / DP;
   float o0[G], o1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { o0[h] = 0.f; o1[h] = 0.f; }
-  const float scale = 1.0f / sqrtf((float)D);
-  const bf16_t* kbase = tab.k[seq] + (size_t)g * D;
-  const uint32_t* vbase = (const uint32_t*)(tab.v[seq] + (size_t)g * D) + dp;
   __syncthreads();
 
   for (int s0 = start; s0 < end; s0 += SUB) {
     const int nk = min(SUB, end - s0);
     // scores: lanes 4k..4k+3 share slot k, each over D/4 dims
     {
-      const int k = tid >> 2, qq = tid & 3;
       float s[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) s[h] = 0.f;
-      if (k < nk) {
-        const u32x4_t* krow = (const u32x4_t*)(kbase + (size_t)(s0 + k) * kvd + qq * DQ);
+      if (kslot < nk) {
 #pragma unroll
         for (int j = 0; j < DQ / 8; ++j) {
-          u32x4_t kv = krow[j];
+          const u32x4_t kv = kreg[j];
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             const u32x4_t qv = *(const u32x4_t*)&qs[h][qq * (DQ / 2) + 4 * j];
@@ -98,7 +119,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
         float t = s[h];
         t += __shfl_xor(t, 1, WAVE);
         t += __shfl_xor(t, 2, WAVE);
-        if (qq == 0) S[h][k] = k < nk ? t * scale : -INFINITY;
+        if (qq == 0) S[h][kslot] = kslot < nk ? t * scale : -INFINITY;
       }
     }
     __syncthreads();
@@ -125,14 +146,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
       o0[h] *= As[h];
       o1[h] *= As[h];
     }
-    // all of this lane's value loads are issued before any is used
-    constexpr int KPL = SUB / NG;  // slots per lane
-    uint32_t vv[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int k = grp + i * NG;
-      vv[i] = k < nk ? vbase[(size_t)(s0 + k) * (kvd / 2)] : 0u;
-    }
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
       const int k = grp + i * NG;
@@ -145,6 +158,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
         o1[h] = fmaf(e, v1, o1[h]);
       }
     }
+    if (s0 + SUB < end) issue(s0 + SUB);
     __syncthreads();  // S is rewritten by the next sub-block
   }
 
@@ -180,6 +194,10 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
   const int p = tab.pos0[seq] + rt % tab.rows_per_seq;
   const int nb = p / block_slots(p) + 1;
   const float* pp = part + ((size_t)rt * nq + h) * MAXB * (D + 2);
+  // every load of the row is issued before the first is needed
+  float ob[MAXB];
+#pragma unroll
+  for (int b = 0; b < MAXB; ++b) ob[b] = b < nb ? pp[(size_t)b * (D + 2) + 2 + j] : 0.f;
   if (j < nb) {
     wts[j] = pp[(size_t)j * (D + 2)];
     lsum[j] = pp[(size_t)j * (D + 2) + 1];
@@ -191,11 +209,13 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
   if (j < nb) wts[j] = expf(wts[j] - M);
   __syncthreads();
   float L = 0.f, O = 0.f;
-#pragma unroll 8
-  for (int b = 0; b < nb; ++b) {
-    const float w = wts[b];
-    L = fmaf(lsum[b], w, L);
-    O = fmaf(pp[(size_t)b * (D + 2) + 2 + j], w, O);
+#pragma unroll
+  for (int b = 0; b < MAXB; ++b) {
+    if (b < nb) {
+      const float w = wts[b];
+      L = fmaf(lsum[b], w, L);
+      O = fmaf(ob[b], w, O);
+    }
   }
   out[((size_t)rt * nq + h) * D + j] = f2bf(O / L);
 }

@@ -13,6 +13,11 @@
 #include "common.h"
 #include "launch.h"
 
+// Weight rows are streamed once per step: nontemporal loads.
+#ifndef GEMV_WLOAD
+#define GEMV_WLOAD(p) __builtin_nontemporal_load(p)
+#endif
+
 struct GemvArgs {
   GemvSeg seg[3];
   int nseg;
@@ -36,7 +41,7 @@ __device__ __forceinline__ float silu_bf16(float g) { return rbf(g / (1.0f + exp
 
 // NR weight rows per wave; for SWIGLU the first NR/2 come from the gate
 // matrix and the last NR/2 from the up matrix, for the same output columns.
-template <int R, int NR, int EPI, bool NORM, bool XLDS>
+template <int R, int NR, int EPI, bool NORM, bool XLDS, int P>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   extern __shared__ u32x4_t sx[];  // XLDS: the (normalised) input rows, [R][K/8]
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
@@ -87,14 +92,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int nv = a.K >> 3;
   const u32x4_t* xb = (const u32x4_t*)a.x;
   const int xs = a.ldx >> 3;
-  // Software pipeline: the weight vectors of the next step are in flight
-  // while this step's are consumed; the first step's loads are issued before
-  // the norm prologue so its row reads overlap them.
-  u32x4_t wn[NR];
-  if (lane < nv) {
+  // Software pipeline, P steps deep: the weight vectors of the next P steps
+  // are in flight while this step's are consumed; the first loads are issued
+  // before the norm prologue so its row reads overlap them.  The partial sums
+  // still take the vectors v = lane, lane + 64, ... in order.
+  u32x4_t wq[P][NR];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) wn[i] = __builtin_nontemporal_load(wp[i] + lane);
-  }
+  for (int p = 0; p < P; ++p)
+    if (lane + p * WAVE < nv) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) wq[p][i] = GEMV_WLOAD(wp[i] + lane + p * WAVE);
+    }
   float rs[R];
   if (NORM) {
 #pragma unroll
@@ -110,33 +118,38 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     }
     __syncthreads();
   }
-  for (int v = lane; v < nv; v += WAVE) {
-    u32x4_t w[NR];
+  for (int v0 = lane; v0 < nv; v0 += P * WAVE) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) w[i] = wn[i];
-    if (v + WAVE < nv) {
+    for (int p = 0; p < P; ++p) {
+      const int v = v0 + p * WAVE;
+      if (v >= nv) break;
+      u32x4_t w[NR];
 #pragma unroll
-      for (int i = 0; i < NR; ++i) wn[i] = __builtin_nontemporal_load(wp[i] + v + WAVE);
-    }
-    u32x4_t g;
-    if (NORM && !XLDS) g = nw[v];
+      for (int i = 0; i < NR; ++i) w[i] = wq[p][i];
+      if (v + P * WAVE < nv) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      u32x4_t xv;
-      if (XLDS) {
-        xv = sx[r * nv + v];
-      } else {
-        xv = xb[r * xs + v];
-        if (NORM) xv = norm8(xv, g, rs[r]);
+        for (int i = 0; i < NR; ++i) wq[p][i] = GEMV_WLOAD(wp[i] + v + P * WAVE);
       }
+      u32x4_t g;
+      if (NORM && !XLDS) g = nw[v];
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        float t = acc[i][r];
-        t = dot2(w[i].x, xv.x, t);
-        t = dot2(w[i].y, xv.y, t);
-        t = dot2(w[i].z, xv.z, t);
-        t = dot2(w[i].w, xv.w, t);
-        acc[i][r] = t;
+      for (int r = 0; r < R; ++r) {
+        u32x4_t xv;
+        if (XLDS) {
+          xv = sx[r * nv + v];
+        } else {
+          xv = xb[r * xs + v];
+          if (NORM) xv = norm8(xv, g, rs[r]);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          float t = acc[i][r];
+          t = dot2(w[i].x, xv.x, t);
+          t = dot2(w[i].y, xv.y, t);
+          t = dot2(w[i].z, xv.z, t);
+          t = dot2(w[i].w, xv.w, t);
+          acc[i][r] = t;
+        }
       }
     }
   }
@@ -203,16 +216,18 @@ constexpr int GEMV_XLDS_BYTES = 64 * 1024;
 template <int R, int EPI, bool NORM>
 static void launch_r(const GemvArgs& a, int N, hipStream_t s) {
   // weight rows per wave: more for small windows (more bytes in flight per
-  // wave), fewer for large ones (register budget of the R*NR partials).
+  // wave), fewer for large ones (register budget of the R*NR partials); the
+  // prefetch depth shrinks with the window for the same reason.
   constexpr int NR = EPI == GEMV_QKV_ROPE ? 4
                      : EPI == GEMV_SWIGLU ? (R <= 4 ? 4 : 2) : (R <= 2 ? 4 : 2);
+  constexpr int P = R == 1 ? 4 : R <= 4 ? 2 : 1;
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
   int grid = N / (4 * COLS);
   const size_t xbytes = (size_t)R * a.K * 2;
   if (xbytes <= GEMV_XLDS_BYTES)
-    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, true>), dim3(grid), dim3(256), xbytes, s, a);
+    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, true, P>), dim3(grid), dim3(256), xbytes, s, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, false>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, false, P>), dim3(grid), dim3(256), 0, s, a);
 }
 
 // Inputs are normalised inside the projection for windows of up to

@@ -4,18 +4,21 @@
 //
 // One workgroup = one query head and 128 chunk rows (4 waves x 32 rows).  Key
 // tiles of 64 cache slots are staged in LDS (keys [slot][d], values
-// transposed [d][slot]) and shared by the four waves.  Per 32-key sub-tile a
-// wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as rows,
-// queries as columns, so each lane holds 16 scores of one query and the
-// softmax reductions stay in registers plus one xor-32 exchange), updates the
-// running max and sum in fp32 (online softmax), and accumulates
-// O^T += V^T P^T.  The probabilities enter that product as the sum of two
-// bf16 parts (hi = bf16(p), lo = bf16(p - hi): two MFMAs), which keeps about
-// 16 significant bits of each weight; the query rows' running state and the
-// output accumulators are fp32, and the output is rounded once to bf16.
-// The P^T operand is the S^T accumulator registers themselves: an MFMA sums
-// over its k slots in any order, so V^T is read in the key order those
-// registers hold.
+// transposed [d][slot]), double-buffered: the next tile's global loads are in
+// flight while the current tile is consumed.  Per tile a wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as rows, queries as
+// columns, so each lane holds 32 scores of one query and the softmax
+// reductions stay in registers plus one xor-32 exchange), updates the running
+// max and sum in fp32 (online softmax, in base 2 with the 1/sqrt(d) scale
+// folded into the exponent), and accumulates O^T += V^T P^T.  The
+// probabilities enter that product as the sum of two bf16 parts (hi =
+// bf16(p), lo = bf16(p - hi): two MFMAs), which keeps about 16 significant
+// bits of each weight; the query rows' running state and the output
+// accumulators are fp32, and the output is rounded once to bf16.  The P^T
+// operand is the S^T accumulator registers themselves: an MFMA sums over its
+// k slots in any order, so V^T is read in the key order those registers hold.
+// The causal mask is applied only on tiles that reach past a wave's first
+// query.
 #include "common.h"
 #include "launch.h"
 
@@ -25,6 +28,17 @@ constexpr int QT = 128;  // chunk rows per workgroup
 constexpr int KT = 64;   // cache slots per LDS tile
 constexpr int VPAD = 4;
 
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+  bf2 v = {(__bf16)a, (__bf16)b};  // v_cvt_pk_bf16_f32: round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// nonzero when either bf16 half of w has an all-ones exponent (Inf or NaN)
+__device__ __forceinline__ uint32_t nonfinite2(uint32_t w) {
+  return ((w & 0x7F807F80u) + 0x00800080u) & 0x80008000u;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restrict__ q,
                                                            const bf16_t* __restrict__ kc,
@@ -33,20 +47,28 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restr
                                                            bf16_t* __restrict__ out) {
   constexpr int KLD = D + 8;
   constexpr int VLD = KT + VPAD;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[KT * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[D * VLD];
-  __shared__ int sBad[KT];  // slot holds a non-finite value
+  constexpr int KCH = KT * D / 8 / 256;   // 16-byte key chunks per thread per tile
+  constexpr int DCH = D / 8;              // 16-byte chunks per slot
+  constexpr int VS = KT * DCH / 256;      // value slots per thread per tile
+  static_assert(VS == 2 || VS == 4, "value staging takes 2 or 4 slots per thread");
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * KLD];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][D * VLD];
+  __shared__ int sBad[2][KT];   // slot holds a non-finite value
+  __shared__ int sBadW[2][4];   // some slot of the tile does (per staging wave)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // heaviest row blocks first: block x covers rows of block (nblk - 1 - x)
+  const int rb = gridDim.x - 1 - blockIdx.x;
   const int h = blockIdx.y, g = h / (nq / nkv);
-  const int r0 = blockIdx.x * QT;
+  const int r0 = rb * QT;
   const int lq = lane & 31, half = lane >> 5;
   const int qrow = r0 + wave * 32 + lq;               // this lane's query row in the chunk
   const int qpos = pos0 + min(qrow, rows - 1);         // its absolute position
+  const int wave_first = pos0 + min(r0 + wave * 32, rows - 1);
   const int wave_last = pos0 + min(r0 + wave * 32 + 31, rows - 1);
   const int block_last = pos0 + min(r0 + QT - 1, rows - 1);
   const int kvd = nkv * D;
-  const float scale = 1.0f / sqrtf((float)D);
+  const float c2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
 
   // Q^T fragments: lane holds q[qrow][16t + 8*half .. +8] for t < D/16
   bf16x8_t qf[D / 16];
@@ -56,6 +78,82 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restr
     for (int t = 0; t < D / 16; ++t) qf[t] = *(const bf16x8_t*)(src + 16 * t);
   }
 
+  // staging: keys as KCH chunks (slot c/DCH, dims (c%DCH)*8), values as VS
+  // consecutive slots VS*(tid/DCH) .. at dims (tid%DCH)*8
+  const int vslot = VS * (tid / DCH), vdc = (tid % DCH) * 8;
+  u32x4_t rk[KCH], rv[VS];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * 256, p = k0 + c / DCH;
+      rk[i] = p <= block_last ? *(const u32x4_t*)(kc + (size_t)p * kvd + g * D + (c % DCH) * 8)
+                              : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < VS; ++j) {
+      const int p = k0 + vslot + j;
+      rv[j] = p <= block_last ? *(const u32x4_t*)(vc + (size_t)p * kvd + g * D + vdc)
+                              : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  // Values are staged transposed.  A masked slot still meets a zero weight in
+  // the value product, and 0 * NaN would leak into earlier rows, so
+  // non-finite values are staged as zero and their slot flagged: a score
+  // against a flagged slot that is not masked becomes NaN, which is what the
+  // rows attending to it would get.
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * 256;
+      *(u32x4_t*)&sK[buf][(c / DCH) * KLD + (c % DCH) * 8] = rk[i];
+    }
+    uint32_t badj[VS];
+    uint32_t any = 0;
+#pragma unroll
+    for (int j = 0; j < VS; ++j) {
+      badj[j] = nonfinite2(rv[j].x) | nonfinite2(rv[j].y) | nonfinite2(rv[j].z) | nonfinite2(rv[j].w);
+      any |= badj[j];
+    }
+    if (any) {  // rare: zero the non-finite halves
+#pragma unroll
+      for (int j = 0; j < VS; ++j) {
+        uint32_t w[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((w[e] & 0x7F80u) == 0x7F80u) w[e] &= 0xFFFF0000u;
+          if ((w[e] & 0x7F800000u) == 0x7F800000u) w[e] &= 0x0000FFFFu;
+        }
+        rv[j] = u32x4_t{w[0], w[1], w[2], w[3]};
+      }
+    }
+    // transpose VS slots x eight dims into eight rows of sV
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // dims vdc + 2e (low halves) and vdc + 2e + 1 (high halves)
+      const uint32_t w0 = rv[0][e], w1 = rv[1][e];
+      const uint32_t lo01 = (w0 & 0xFFFFu) | (w1 << 16), hi01 = (w0 >> 16) | (w1 & 0xFFFF0000u);
+      if (VS == 4) {
+        const uint32_t w2 = rv[VS > 2 ? 2 : 0][e], w3 = rv[VS > 2 ? 3 : 0][e];
+        const uint32_t lo23 = (w2 & 0xFFFFu) | (w3 << 16), hi23 = (w2 >> 16) | (w3 & 0xFFFF0000u);
+        *(uint2*)&sV[buf][(vdc + 2 * e) * VLD + vslot] = make_uint2(lo01, lo23);
+        *(uint2*)&sV[buf][(vdc + 2 * e + 1) * VLD + vslot] = make_uint2(hi01, hi23);
+      } else {
+        *(uint32_t*)&sV[buf][(vdc + 2 * e) * VLD + vslot] = lo01;
+        *(uint32_t*)&sV[buf][(vdc + 2 * e + 1) * VLD + vslot] = hi01;
+      }
+    }
+    // a slot's flag is the OR over the DCH threads holding its dims
+#pragma unroll
+    for (int j = 0; j < VS; ++j) {
+      uint32_t f = badj[j];
+#pragma unroll
+      for (int m = 1; m < DCH; m <<= 1) f |= __shfl_xor(f, m, WAVE);
+      if (vdc == 0) sBad[buf][vslot + j] = f != 0;
+    }
+    const int wany = __any(any != 0);
+    if (lane == 0) sBadW[buf][wave] = wany;
+  };
+
   f32x16_t acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i)
@@ -64,106 +162,90 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restr
   float mrow = -INFINITY, lrow = 0.f;
 
   const int ntiles = block_last / KT + 1;
+  gload(0);
+  lstore(0);
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int k0 = kt * KT;
-    __syncthreads();  // previous tile's readers are done
-    if (tid < KT) sBad[tid] = 0;
-    __syncthreads();
-    // Stage keys [slot][d] and values transposed [d][slot].  Slots past the
-    // block's last query are zero (their scores are masked).  A masked slot
-    // still meets a zero weight in the value product, and 0 * NaN would leak
-    // into earlier rows, so non-finite values are staged as zero and their
-    // slot flagged: a score against a flagged slot that is not masked becomes
-    // NaN, which is what the rows attending to it would get.
-    for (int c = tid; c < KT * D / 8; c += 256) {
-      int slot = c / (D / 8), dc = (c % (D / 8)) * 8;
-      int p = k0 + slot;
-      u32x4_t kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (p <= block_last) {
-        kv = *(const u32x4_t*)(kc + (size_t)p * kvd + g * D + dc);
-        vv = *(const u32x4_t*)(vc + (size_t)p * kvd + g * D + dc);
+    const int k0 = kt * KT, buf = kt & 1;
+    if (kt + 1 < ntiles) gload(k0 + KT);
+    if (k0 <= wave_last) {
+      // S^T = K Q^T for 64 keys (two 32-key halves) x 32 queries
+      f32x16_t s[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[u][r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          bf16x8_t kf = *(const bf16x8_t*)&sK[buf][(32 * u + lq) * KLD + 16 * t + 8 * half];
+          s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[u], 0, 0, 0);
+        }
       }
-      *(u32x4_t*)&sK[slot * KLD + dc] = kv;
-      uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-      int bad = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bf16_t lo = (bf16_t)(w[e] & 0xFFFF), hi = (bf16_t)(w[e] >> 16);
-        if ((lo & 0x7F80) == 0x7F80) { bad = 1; lo = 0; }
-        if ((hi & 0x7F80) == 0x7F80) { bad = 1; hi = 0; }
-        sV[(dc + 2 * e) * VLD + slot] = lo;
-        sV[(dc + 2 * e + 1) * VLD + slot] = hi;
-      }
-      if (bad) sBad[slot] = 1;
-    }
-    __syncthreads();
-    if (k0 > wave_last) continue;  // every key of this tile is after this wave's queries
-
-#pragma unroll
-    for (int sub = 0; sub < KT; sub += 32) {
-      const int ks = k0 + sub;
-      if (ks > wave_last) break;
-      // S^T = K Q^T for 32 keys x 32 queries
-      f32x16_t s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        bf16x8_t kf = *(const bf16x8_t*)&sK[(sub + lq) * KLD + 16 * t + 8 * half];
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s, 0, 0, 0);
-      }
-      // scale, causal mask, tile max (keys of reg r: ks + 8*(r/4) + 4*half + r%4)
+      // keys of register r of half u: k0 + 32u + 8*(r/4) + 4*half + r%4
+      const bool any_bad = sBadW[buf][0] | sBadW[buf][1] | sBadW[buf][2] | sBadW[buf][3];
+      const bool diag = k0 + KT - 1 > wave_first;
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int kp = ks + 8 * (r >> 2) + 4 * half + (r & 3);
-        float v = kp <= qpos ? (sBad[kp - k0] ? NAN : s[r] * scale) : -INFINITY;
-        s[r] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = s[u][r] * c2;
+          const int ko = 32 * u + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (any_bad && sBad[buf][ko]) v = NAN;
+          if (diag && k0 + ko > qpos) v = -INFINITY;
+          s[u][r] = v;
+          mx = fmaxf(mx, v);
+        }
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
       const float mnew = fmaxf(mrow, mx);
       // a row with no unmasked key yet keeps zero weights
-      const float alpha = mnew == -INFINITY ? 1.f : expf(mrow - mnew);
-      // p = hi + lo with hi = bf16(p), lo = bf16(p - hi): about 16 significant
-      // bits of each weight reach the matrix product
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mref);
+      // p = hi + lo with hi = bf16(p), lo = bf16(p - hi)
       float psum = 0.f;
-      uint32_t pk[8], pl[8];
+      uint32_t pk[16], pl[16];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0 = mnew == -INFINITY ? 0.f : expf(s[r] - mnew);
-        float p1 = mnew == -INFINITY ? 0.f : expf(s[r + 1] - mnew);
-        bf16_t h0 = f2bf(p0), h1 = f2bf(p1);
-        psum += p0 + p1;
-        pk[r / 2] = pack_bf2(h0, h1);
-        pl[r / 2] = pack_bf2(f2bf(p0 - bf2f(h0)), f2bf(p1 - bf2f(h1)));
-      }
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(s[u][r] - mref);
+          const float p1 = __builtin_amdgcn_exp2f(s[u][r + 1] - mref);
+          psum += p0;
+          psum += p1;
+          const uint32_t hw = cvt_pk_bf16(p0, p1);
+          pk[8 * u + r / 2] = hw;
+          pl[8 * u + r / 2] = cvt_pk_bf16(p0 - __uint_as_float(hw << 16),
+                                          p1 - __uint_as_float(hw & 0xFFFF0000u));
+        }
       psum += __shfl_xor(psum, 32, WAVE);
       lrow = lrow * alpha + psum;
       mrow = mnew;
+      if (!__all(alpha == 1.f)) {
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i)
+        for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
-      // O^T += V^T P^T, two k-steps of 16 keys; k slot 8*half + i holds key
-      // 16*st + 8*(i/4) + 4*half + i%4 (the S^T register order)
+          for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+      }
+      // O^T += V^T P^T in four k-steps of 16 keys; k slot 8*half + i of step
+      // st holds key 16*st + 8*(i/4) + 4*half + i%4 (the S^T register order)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        u32x4_t pw = {pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]};
-        u32x4_t plw = {pl[4 * st], pl[4 * st + 1], pl[4 * st + 2], pl[4 * st + 3]};
-        bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-        bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, plw);
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8_t pf = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]});
+        const bf16x8_t pfl = __builtin_bit_cast(
+            bf16x8_t, u32x4_t{pl[4 * st], pl[4 * st + 1], pl[4 * st + 2], pl[4 * st + 3]});
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
-          const bf16_t* vrow = &sV[(i * 32 + lq) * VLD + sub + 16 * st + 4 * half];
-          uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 8);
-          u32x4_t vw = {lo.x, lo.y, hi.x, hi.y};
-          bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vw);
+          const bf16_t* vrow = &sV[buf][(i * 32 + lq) * VLD + 16 * st + 4 * half];
+          const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 8);
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[i], 0, 0, 0);
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfl, acc[i], 0, 0, 0);
         }
       }
     }
+    if (kt + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
   }
 
   // O = O^T / l: lane holds column qrow, rows d = 32i + 8(r/4) + 4*half + r%4

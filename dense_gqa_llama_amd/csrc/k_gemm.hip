@@ -40,8 +40,17 @@ struct GemmArgs {
 
 __device__ __forceinline__ float silu_r(float g) { return rbf(g / (1.0f + expf(-g))); }
 
+// Workgroup b runs on XCD b % 8; tiles are handed out so that each XCD
+// takes a contiguous run of tile indices, and within a run the row tiles of
+// one column tile are adjacent: the weight slice of a column tile is then
+// fetched into one XCD's L2 and shared by the row tiles running beside it.
+__device__ __forceinline__ int xcd_tile(int b, int nt) {
+  const int full = nt / 8 * 8;
+  return b < full ? (b % 8) * (nt / 8) + b / 8 : b;
+}
+
 template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a, int mtiles) {
   constexpr int NWN = BN / WN;
   constexpr int NT = (BM / WM) * NWN * 64;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -49,23 +58,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   static_assert(A_LD * NT == BM * 8 && B_LD * NT == BN * 8, "tile / thread mismatch");
   static_assert(EPI != GEMV_SWIGLU || WN % 64 == 0, "SWIGLU pairs 32-column tiles");
 
-  __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * LDK];
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  bf16_t* sA0 = smem;
+  bf16_t* sB0 = smem + 2 * BM * LDK;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (t % mtiles) * BM, n0 = (t / mtiles) * BN;
 
   // global sources of this thread's chunks
   const bf16_t* srcA[A_LD];
   const bf16_t* srcB[B_LD];
-  int offA[A_LD], offB[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     int c = tid + i * NT, row = c >> 3, kc = c & 7;
     int m = min(m0 + row, a.M - 1);
     srcA[i] = a.A + (size_t)m * a.lda + kc * 8;
-    offA[i] = row * LDK + kc * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
@@ -83,8 +92,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       w = W + (size_t)(col - base) * a.K;
     }
     srcB[i] = w + kc * 8;
-    offB[i] = row * LDK + kc * 8;
   }
+  const int st_off = (tid >> 3) * LDK + (tid & 7) * 8;  // LDS offset of chunk i: + i*(NT/8)*LDK
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -102,10 +111,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
     for (int i = 0; i < B_LD; ++i) rb[i] = __builtin_nontemporal_load((const u32x4_t*)(srcB[i] + kt * BK));
   };
   auto lstore = [&](int buf) {
+    bf16_t* sA = sA0 + buf * BM * LDK;
+    bf16_t* sB = sB0 + buf * BN * LDK;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) *(u32x4_t*)&sA[buf][offA[i]] = ra[i];
+    for (int i = 0; i < A_LD; ++i) *(u32x4_t*)&sA[st_off + i * (NT / 8) * LDK] = ra[i];
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) *(u32x4_t*)&sB[buf][offB[i]] = rb[i];
+    for (int i = 0; i < B_LD; ++i) *(u32x4_t*)&sB[st_off + i * (NT / 8) * LDK] = rb[i];
   };
 
   const int nk = a.K / BK;
@@ -113,23 +124,34 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   lstore(0);
   __syncthreads();
   const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int fa_off = (wm * WM + lr) * LDK + lk, fb_off = (wn * WN + lr) * LDK + lk;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
+    const bf16_t* sA = sA0 + buf * BM * LDK + fa_off;
+    const bf16_t* sB = sB0 + buf * BN * LDK + fb_off;
+    // fragments of step kk + 16 are read while step kk's products run
+    bf16x8_t fa[2][TM], fb[2][TN];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8_t fa[TM], fb[TN];
+    for (int i = 0; i < TM; ++i) fa[0][i] = *(const bf16x8_t*)&sA[i * 32 * LDK];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        fa[i] = *(const bf16x8_t*)&sA[buf][(wm * WM + i * 32 + lr) * LDK + kk + lk];
+    for (int j = 0; j < TN; ++j) fb[0][j] = *(const bf16x8_t*)&sB[j * 32 * LDK];
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        fb[j] = *(const bf16x8_t*)&sB[buf][(wn * WN + j * 32 + lr) * LDK + kk + lk];
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          fa[cur ^ 1][i] = *(const bf16x8_t*)&sA[i * 32 * LDK + (ks + 1) * 16];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          fb[cur ^ 1][j] = *(const bf16x8_t*)&sB[j * 32 * LDK + (ks + 1) * 16];
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < nk) lstore(buf ^ 1);
     __syncthreads();
@@ -171,14 +193,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 
 template <int BM, int BN, int WM, int WN, int EPI>
 void launch_tile(const GemmArgs& a, int ncols, hipStream_t s) {
-  dim3 grid(ncols / BN, (a.M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), grid, dim3((BM / WM) * (BN / WN) * 64),
-                     0, s, a);
+  const int mtiles = (a.M + BM - 1) / BM;
+  const int nt = (ncols / BN) * mtiles;
+  const size_t lds = (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t);
+  static bool attr = false;  // one-time opt-in above the default dynamic LDS limit
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)gemm_kernel<BM, BN, WM, WN, EPI>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3(nt),
+                     dim3((BM / WM) * (BN / WN) * 64), lds, s, a, mtiles);
 }
 
 }  // namespace
 
-// ncols: tile columns (N, or 2F for SWIGLU); a multiple of 128.
+// ncols: tile columns (N, or 2F for SWIGLU); a multiple of 128.  Widths that
+// are multiples of 256 take 256 x 256 tiles (eight waves of 128 x 64), which
+// halve the LDS and L2 traffic per product of the 128 x 128 tiles; the split
+// of K into 16-deep MFMA steps, and so every output's bits, is the same for
+// both.
 void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* seg, int nseg,
                  const void* gate, const void* up, void* out, int ldo, float* out32, int ld32,
                  int ncols, hipStream_t s) {
@@ -195,7 +229,15 @@ void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* s
   a.ldo = ldo;
   a.out32 = out32;
   a.ld32 = ld32;
-  if (epi == GEMV_STORE) launch_tile<128, 128, 64, 64, GEMV_STORE>(a, ncols, s);
-  else if (epi == GEMV_RESIDUAL) launch_tile<128, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
-  else launch_tile<128, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
+  const bool big = ncols % 256 == 0;
+  if (epi == GEMV_STORE) {
+    if (big) launch_tile<256, 256, 128, 64, GEMV_STORE>(a, ncols, s);
+    else launch_tile<128, 128, 64, 64, GEMV_STORE>(a, ncols, s);
+  } else if (epi == GEMV_RESIDUAL) {
+    if (big) launch_tile<256, 256, 128, 64, GEMV_RESIDUAL>(a, ncols, s);
+    else launch_tile<128, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
+  } else {
+    if (big) launch_tile<256, 256, 128, 64, GEMV_SWIGLU>(a, ncols, s);
+    else launch_tile<128, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
+  }
 }

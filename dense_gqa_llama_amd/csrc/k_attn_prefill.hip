@@ -40,7 +40,7 @@ __device__ __forceinline__ uint32_t nonfinite2(uint32_t w) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __restrict__ q,
                                                            const bf16_t* __restrict__ kc,
                                                            const bf16_t* __restrict__ vc,
                                                            int rows, int pos0, int nq, int nkv,
@@ -82,18 +82,18 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restr
   // consecutive slots VS*(tid/DCH) .. at dims (tid%DCH)*8
   const int vslot = VS * (tid / DCH), vdc = (tid % DCH) * 8;
   u32x4_t rk[KCH], rv[VS];
+  // Slots past the block's last query are masked for every row of the block;
+  // their loads are clamped to that last slot (a valid cache row).
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * 256, p = k0 + c / DCH;
-      rk[i] = p <= block_last ? *(const u32x4_t*)(kc + (size_t)p * kvd + g * D + (c % DCH) * 8)
-                              : u32x4_t{0u, 0u, 0u, 0u};
+      const int c = tid + i * 256, p = min(k0 + c / DCH, block_last);
+      rk[i] = *(const u32x4_t*)(kc + (size_t)p * kvd + g * D + (c % DCH) * 8);
     }
 #pragma unroll
     for (int j = 0; j < VS; ++j) {
-      const int p = k0 + vslot + j;
-      rv[j] = p <= block_last ? *(const u32x4_t*)(vc + (size_t)p * kvd + g * D + vdc)
-                              : u32x4_t{0u, 0u, 0u, 0u};
+      const int p = min(k0 + vslot + j, block_last);
+      rv[j] = *(const u32x4_t*)(vc + (size_t)p * kvd + g * D + vdc);
     }
   };
   // Values are staged transposed.  A masked slot still meets a zero weight in
@@ -184,41 +184,30 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restr
       // keys of register r of half u: k0 + 32u + 8*(r/4) + 4*half + r%4
       const bool any_bad = sBadW[buf][0] | sBadW[buf][1] | sBadW[buf][2] | sBadW[buf][3];
       const bool diag = k0 + KT - 1 > wave_first;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[u][r] *= c2;
+      if (any_bad | diag) {  // tiles on the diagonal, or holding a non-finite value
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = 32 * u + 8 * (r >> 2) + 4 * half + (r & 3);
+            float v = sBad[buf][ko] ? NAN : s[u][r];
+            s[u][r] = k0 + ko > qpos ? -INFINITY : v;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[u][r] * c2;
-          const int ko = 32 * u + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (any_bad && sBad[buf][ko]) v = NAN;
-          if (diag && k0 + ko > qpos) v = -INFINITY;
-          s[u][r] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
       const float mnew = fmaxf(mrow, mx);
       // a row with no unmasked key yet keeps zero weights
       const float mref = mnew == -INFINITY ? 0.f : mnew;
       const float alpha = __builtin_amdgcn_exp2f(mrow - mref);
-      // p = hi + lo with hi = bf16(p), lo = bf16(p - hi)
-      float psum = 0.f;
-      uint32_t pk[16], pl[16];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(s[u][r] - mref);
-          const float p1 = __builtin_amdgcn_exp2f(s[u][r + 1] - mref);
-          psum += p0;
-          psum += p1;
-          const uint32_t hw = cvt_pk_bf16(p0, p1);
-          pk[8 * u + r / 2] = hw;
-          pl[8 * u + r / 2] = cvt_pk_bf16(p0 - __uint_as_float(hw << 16),
-                                          p1 - __uint_as_float(hw & 0xFFFF0000u));
-        }
-      psum += __shfl_xor(psum, 32, WAVE);
-      lrow = lrow * alpha + psum;
       mrow = mnew;
       if (!__all(alpha == 1.f)) {
 #pragma unroll
@@ -227,13 +216,24 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restr
           for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
       }
       // O^T += V^T P^T in four k-steps of 16 keys; k slot 8*half + i of step
-      // st holds key 16*st + 8*(i/4) + 4*half + i%4 (the S^T register order)
+      // st holds key 16*st + 8*(i/4) + 4*half + i%4 (the S^T register order).
+      // p = hi + lo with hi = bf16(p), lo = bf16(p - hi).
+      float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const bf16x8_t pf = __builtin_bit_cast(
-            bf16x8_t, u32x4_t{pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]});
-        const bf16x8_t pfl = __builtin_bit_cast(
-            bf16x8_t, u32x4_t{pl[4 * st], pl[4 * st + 1], pl[4 * st + 2], pl[4 * st + 3]});
+        uint32_t pk[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + 2 * i] - mref);
+          const float p1 = __builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + 2 * i + 1] - mref);
+          psum += p0;
+          psum += p1;
+          const uint32_t hw = cvt_pk_bf16(p0, p1);
+          pk[i] = hw;
+          pl[i] = cvt_pk_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
+        }
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+        const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, u32x4_t{pl[0], pl[1], pl[2], pl[3]});
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
           const bf16_t* vrow = &sV[buf][(i * 32 + lq) * VLD + 16 * st + 4 * half];
@@ -243,6 +243,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const bf16_t* __restr
           acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfl, acc[i], 0, 0, 0);
         }
       }
+      psum += __shfl_xor(psum, 32, WAVE);
+      lrow = lrow * alpha + psum;
     }
     if (kt + 1 < ntiles) lstore(buf ^ 1);
     __syncthreads();

@@ -10,8 +10,11 @@ second, the decode HBM rate against the 8 TB/s peak, the dominant kernel's
 roofline fraction, and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-probe-mib N    # a plain device copy of N MiB, for
+                                          # calibrating HBM byte counters
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -22,6 +25,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# HBM bytes of the dominant kernel from rocprofv3 counters, with the digest of
+# the sources they were taken on (a changed kernel reports no traffic)
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_gate_up_33b_decode_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "dense_gqa_llama_amd", "csrc", f)
+                  for f in ("k_gemv.hip", "common.h", "launch.h")]
 
 
 def log(msg):
@@ -50,6 +58,60 @@ def decode_bytes(g, T):
     written."""
     kvp = g.kv_bytes_per_position()
     return g.decode_weight_bytes() + (T + 1) * kvp + kvp
+
+
+def prefill_gemm_flops(g, rows):
+    """Algorithmic flops of the projections of one prompt chunk (2 per
+    multiply-add; every execution's q/k/v, o, gate/up and down)."""
+    per_exec = g.hidden * (g.q_dim + 2 * g.kv_dim) + g.q_dim * g.hidden + 3 * g.hidden * g.ffn
+    return 2.0 * rows * per_exec * g.n_exec
+
+
+def prefill_attn_flops(g, rows, pos0=0):
+    """Algorithmic flops of causal attention for a chunk at pos0: each row
+    scores and sums its positions (4 d per query head and position)."""
+    pairs = rows * pos0 + rows * (rows + 1) / 2
+    return 4.0 * g.head_dim * g.n_q_heads * pairs * g.n_exec
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is absent or was taken on other sources."""
+    try:
+        fields = {}
+        with open(TRAFFIC_SUMMARY) as fh:
+            for line in fh:
+                if ":" in line and line.startswith("- "):
+                    k, v = line[2:].split(":", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("sources_sha256") != sources_digest():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of mib MiB, three times: its counters
+    read a known number of bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: 3 copies of {n} bytes")
 
 
 def cpu_baseline(g, T, reps=3):
@@ -93,6 +155,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path "
@@ -101,6 +164,9 @@ def main():
 
     ensure_built()
     import torch
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
 
     import dense_gqa_llama_amd as L
     from dense_gqa_llama_amd import binding as B
@@ -169,6 +235,22 @@ def main():
     log(f"gate/up projection: {n} launches, {per_launch_ms * 1e3:.1f} us each, "
         f"{achieved:.0f} GB/s")
 
+    # prompt-chunk projections and attention, each class timed on its own
+    def timed_prefill(kind, launches):
+        B.llama_set_timing(model.handle, kind, launches)
+        request()
+        torch.cuda.synchronize()
+        t, k = B.llama_timing_read(model.handle)
+        B.llama_set_timing(model.handle, "off")
+        return t, k
+    gemm_ms, _ = timed_prefill("prefill_gemm", 4 * g.n_exec)
+    attn_ms, _ = timed_prefill("prefill_attn", g.n_exec)
+    gemm_tf = prefill_gemm_flops(g, P) / (gemm_ms / 1e3) / 1e12
+    attn_tf = prefill_attn_flops(g, P) / (attn_ms / 1e3) / 1e12
+    log(f"prefill projections {gemm_ms:.1f} ms ({gemm_tf:.0f} TFLOP/s), attention "
+        f"{attn_ms:.1f} ms ({attn_tf:.0f} TFLOP/s)")
+    traffic = stored_traffic()
+
     result = {
         "metric": "decode tok/s + HBM GB/s (% peak), 33B bf16 batch 1; prefill tok/s",
         "value": round(dec_tps, 3),
@@ -191,9 +273,17 @@ def main():
         "decode_hbm_gbs": round(dec_gbs, 1),
         "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "prefill_tok_s": round(pre_tps, 1),
+        "prefill_gemm": {"bound": "mfma", "achieved": round(gemm_tf, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "ms_per_chunk": round(gemm_ms, 3)},
+        "prefill_attention": {"bound": "mfma", "achieved": round(attn_tf, 1),
+                              "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "ms_per_chunk": round(attn_ms, 3)},
         "roofline": {"bound": "hbm", "kernel": "decode gate/up projection + SwiGLU (R=1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launch_us": round(per_launch_ms * 1e3, 2)},
     }
     if not args.no_cpu_baseline:

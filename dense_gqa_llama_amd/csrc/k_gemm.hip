@@ -21,8 +21,6 @@
 
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // LDS row stride (bf16): rows land 4 banks apart
 
 struct GemmArgs {
   const bf16_t* A;
@@ -49,13 +47,18 @@ __device__ __forceinline__ int xcd_tile(int b, int nt) {
   return b < full ? (b % 8) * (nt / 8) + b / 8 : b;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a, int mtiles) {
+// Register budget: two waves per SIMD (two workgroups per CU when a
+// workgroup has four waves).
+template <int BM, int BN, int WM, int WN, int EPI, int BK>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, (BM / WM) * (BN / WN) <= 4 ? 2 : 1)
+void gemm_kernel(GemmArgs a, int mtiles) {
+  constexpr int LDK = BK + 8;   // LDS row stride (bf16): 16-byte fragment reads stay conflict-free
+  constexpr int CPR = BK / 8;   // 16-byte chunks per tile row
   constexpr int NWN = BN / WN;
   constexpr int NT = (BM / WM) * NWN * 64;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_LD = BM * 8 / NT, B_LD = BN * 8 / NT;  // 16-byte chunks per thread
-  static_assert(A_LD * NT == BM * 8 && B_LD * NT == BN * 8, "tile / thread mismatch");
+  constexpr int A_LD = BM * CPR / NT, B_LD = BN * CPR / NT;  // 16-byte chunks per thread
+  static_assert(A_LD * NT == BM * CPR && B_LD * NT == BN * CPR, "tile / thread mismatch");
   static_assert(EPI != GEMV_SWIGLU || WN % 64 == 0, "SWIGLU pairs 32-column tiles");
 
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
@@ -72,13 +75,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const bf16_t* srcB[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    int c = tid + i * NT, row = c >> 3, kc = c & 7;
+    int c = tid + i * NT, row = c / CPR, kc = c % CPR;
     int m = min(m0 + row, a.M - 1);
     srcA[i] = a.A + (size_t)m * a.lda + kc * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    int c = tid + i * NT, row = c >> 3, kc = c & 7;
+    int c = tid + i * NT, row = c / CPR, kc = c % CPR;
     int col = n0 + row;  // tile column
     const bf16_t* w;
     if (EPI == GEMV_SWIGLU) {
@@ -93,7 +96,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
     }
     srcB[i] = w + kc * 8;
   }
-  const int st_off = (tid >> 3) * LDK + (tid & 7) * 8;  // LDS offset of chunk i: + i*(NT/8)*LDK
+  const int st_off = (tid / CPR) * LDK + (tid % CPR) * 8;  // chunk i: + i*(NT/CPR)*LDK
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -103,43 +106,52 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4_t ra[A_LD], rb[B_LD];
-  auto gload = [&](int kt) {
+  // Two register sets of staged global loads: the loads of k-tile kt + 2 are
+  // issued while tile kt is consumed and tile kt + 1 waits in the other set,
+  // so a load has two tiles' worth of products to arrive.  Loads past the
+  // last tile are clamped to it (branch-free steps; never consumed).
+  u32x4_t ra[2][A_LD], rb[2][B_LD];
+  auto gload = [&](int set, int kt) {
+    kt = min(kt, a.K / BK - 1);
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *(const u32x4_t*)(srcA[i] + kt * BK);
+    for (int i = 0; i < A_LD; ++i) ra[set][i] = *(const u32x4_t*)(srcA[i] + kt * BK);
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = __builtin_nontemporal_load((const u32x4_t*)(srcB[i] + kt * BK));
+    for (int i = 0; i < B_LD; ++i)
+      rb[set][i] = __builtin_nontemporal_load((const u32x4_t*)(srcB[i] + kt * BK));
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int set, int buf) {
     bf16_t* sA = sA0 + buf * BM * LDK;
     bf16_t* sB = sB0 + buf * BN * LDK;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) *(u32x4_t*)&sA[st_off + i * (NT / 8) * LDK] = ra[i];
+    for (int i = 0; i < A_LD; ++i) *(u32x4_t*)&sA[st_off + i * (NT / CPR) * LDK] = ra[set][i];
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) *(u32x4_t*)&sB[st_off + i * (NT / 8) * LDK] = rb[i];
+    for (int i = 0; i < B_LD; ++i) *(u32x4_t*)&sB[st_off + i * (NT / CPR) * LDK] = rb[set][i];
   };
 
   const int nk = a.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   const int fa_off = (wm * WM + lr) * LDK + lk, fb_off = (wn * WN + lr) * LDK + lk;
-  for (int kt = 0; kt < nk; ++kt) {
+  constexpr int KS = BK / 16;       // MFMA steps per k-tile
+  constexpr int NMF = TM * TN;      // MFMAs per step
+  constexpr int NFR = TM + TN;      // fragment reads per step
+  static_assert(NFR <= NMF, "one fragment read per product");
+
+  // one k-tile: prefetch kt + 2 into `set`, consume kt, stage kt + 1 (other set)
+  auto step = [&](int kt, int set) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    gload(set, kt + 2);
     const bf16_t* sA = sA0 + buf * BM * LDK + fa_off;
     const bf16_t* sB = sB0 + buf * BN * LDK + fb_off;
-    // fragments of step kk + 16 are read while step kk's products run
+    // Fragments of step ks + 1 are read while step ks's products run.
     bf16x8_t fa[2][TM], fb[2][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i) fa[0][i] = *(const bf16x8_t*)&sA[i * 32 * LDK];
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[0][j] = *(const bf16x8_t*)&sB[j * 32 * LDK];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int cur = ks & 1;
-      if (ks + 1 < BK / 16) {
+      if (ks + 1 < KS) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
           fa[cur ^ 1][i] = *(const bf16x8_t*)&sA[i * 32 * LDK + (ks + 1) * 16];
@@ -153,9 +165,43 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
         for (int j = 0; j < TN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    lstore(set ^ 1, buf ^ 1);
+    // pinned order: the global loads first, the first step's fragment reads,
+    // then each step's products interleaved with the next step's reads, the
+    // staged writes riding on the last step
+    __builtin_amdgcn_sched_group_barrier(0x020, A_LD + B_LD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NFR, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS - 1; ++ks) {
+#pragma unroll
+      for (int f = 0; f < NFR; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF - NFR, 0);
+    }
+    constexpr int NW = A_LD + B_LD;
+    constexpr int NP = NW < NMF ? NW : NMF;
+#pragma unroll
+    for (int f = 0; f < NP; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    if (NMF > NP) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NP, 0);
+    if (NW > NP) __builtin_amdgcn_sched_group_barrier(0x200, NW - NP, 0);
     __syncthreads();
+  };
+
+  gload(0, 0);
+  gload(1, 1);
+  lstore(0, 0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, 0);
+    step(kt + 1, 1);
   }
+  if (kt < nk) step(kt, 0);
 
   // epilogue
   const int hrow = (lane >> 5) * 4;
@@ -191,18 +237,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, int BK = 64>
 void launch_tile(const GemmArgs& a, int ncols, hipStream_t s) {
   const int mtiles = (a.M + BM - 1) / BM;
   const int nt = (ncols / BN) * mtiles;
-  const size_t lds = (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t);
+  const size_t lds = (size_t)2 * (BM + BN) * (BK + 8) * sizeof(bf16_t);
   static bool attr = false;  // one-time opt-in above the default dynamic LDS limit
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)gemm_kernel<BM, BN, WM, WN, EPI>,
+    (void)hipFuncSetAttribute((const void*)gemm_kernel<BM, BN, WM, WN, EPI, BK>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3(nt),
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, BK>), dim3(nt),
                      dim3((BM / WM) * (BN / WN) * 64), lds, s, a, mtiles);
 }
 

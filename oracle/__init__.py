@@ -57,6 +57,9 @@ def lib():
         L.orc_residual_add.argtypes = [_P, _P, _I]
         L.orc_argmax.argtypes = [_P, _I]
         L.orc_argmax.restype = ctypes.c_int32
+        L.orc_sample.argtypes = [_P, _I, ctypes.c_double, ctypes.c_int32, ctypes.c_double,
+                                 ctypes.c_double, _P]
+        L.orc_sample.restype = ctypes.c_int32
         L.orc_block.argtypes = [ctypes.POINTER(Geom), ctypes.POINTER(BlockWeights), _P, _P, _I,
                                 _P, _I, _P, _P]
         L.orc_block.restype = ctypes.c_int
@@ -168,6 +171,16 @@ def residual_add(h, y):
 def argmax(logits):
     """Greedy id of one bf16 logit row; -1 when the row holds NaN or +-Inf."""
     return int(lib().orc_argmax(_u16(logits).ctypes.data, logits.size))
+
+
+def sample(logits, temperature, top_k, top_p, u):
+    """Seeded top-k / top-p draw from one row of bf16 logits against the
+    uniform ``u``; returns (token id or -1, decision margin)."""
+    logits = _u16(logits)
+    m = np.zeros(1, dtype=np.float64)
+    t = lib().orc_sample(logits.ctypes.data, logits.size, float(temperature), int(top_k),
+                         float(top_p), float(u), m.ctypes.data)
+    return int(t), float(m[0])
 
 
 def block(geom, w, kc, vc, pos, h, want_mid=False):

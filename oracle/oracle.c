@@ -238,6 +238,81 @@ int32_t orc_argmax(const uint16_t* logits, int64_t V) {
   return best;
 }
 
+/* Seeded sampling over bf16 logits (issue "A llama family on Metal", the
+ * served sampling checks; pull request, section "How": tokens drawn on the
+ * GPU; model card "Nanbeige4.3-33B EXL3", upstream's recommended temperature,
+ * top_p and top_k).  Hugging Face's logits warpers in their default order --
+ * temperature, top-k, top-p -- then one draw against the uniform u in [0, 1):
+ *   1. z_v = logit_v / temperature;
+ *   2. keep the top_k largest z, ordered by value (descending), then id;
+ *   3. p_i = exp(z_i - z_0) / sum_j exp(z_j - z_0) over the kept;
+ *   4. top-p: candidate i stays while the probability of the candidates
+ *      before it is below top_p (the first always stays);
+ *   5. the first remaining candidate whose cumulative probability, over the
+ *      remaining ones renormalised, exceeds u.
+ * A row holding NaN or +-Inf is refused (-1).  *margin (nullable) receives
+ * the smallest distance, relative to the sum it is taken against, between a
+ * decision threshold (the top-p cut, the draw target) and the cumulative sum
+ * compared with it: a perturbation of the weights smaller than that cannot
+ * change the token. */
+int32_t orc_sample(const uint16_t* logits, int64_t V, double temperature, int32_t top_k,
+                   double top_p, double u, double* margin) {
+  if (top_k < 1 || V < 1 || !(temperature > 0.0)) return -1;
+  int64_t k = top_k < V ? top_k : V;
+  int32_t* id = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  double* val = (double*)malloc(sizeof(double) * (size_t)k);
+  double* e = (double*)malloc(sizeof(double) * (size_t)k);
+  int64_t n_in = 0;
+  int32_t tok = -1;
+  for (int64_t v = 0; v < V; ++v) {
+    double x = orc_f64(logits[v]);
+    if (!isfinite(x)) goto done;
+    /* insertion into the kept list (value descending, then id ascending) */
+    if (n_in == k && !(x > val[k - 1])) continue;
+    int64_t pos = n_in < k ? n_in : k - 1;
+    while (pos > 0 && x > val[pos - 1]) {
+      val[pos] = val[pos - 1];
+      id[pos] = id[pos - 1];
+      --pos;
+    }
+    val[pos] = x;
+    id[pos] = (int32_t)v;
+    if (n_in < k) ++n_in;
+  }
+  {
+    double z0 = val[0] / temperature, S = 0.0;
+    for (int64_t i = 0; i < k; ++i) {
+      e[i] = exp(val[i] / temperature - z0);
+      S += e[i];
+    }
+    int64_t n = 1;
+    double cum = e[0];
+    while (n < k && cum < top_p * S) cum += e[n++];
+    double mp = HUGE_VAL;
+    if (n > 1) mp = (top_p * S - (cum - e[n - 1])) / S;
+    if (n < k) mp = fmin(mp, (cum - top_p * S) / S);
+    double target = u * cum, c = 0.0, md = HUGE_VAL;
+    int64_t i = 0;
+    for (; i < n; ++i) {
+      double prev = c;
+      c += e[i];
+      if (c > target) {
+        md = (c - target) / cum;
+        if (i > 0) md = fmin(md, (target - prev) / cum);
+        break;
+      }
+    }
+    if (i == n) i = n - 1;
+    tok = id[i];
+    if (margin) *margin = fmin(mp, md);
+  }
+done:
+  free(id);
+  free(val);
+  free(e);
+  return tok;
+}
+
 /* --------------------------------------------------------------- block --- */
 
 int orc_block(const orc_geom* g, const orc_block_weights* w, uint16_t* kc, uint16_t* vc,

@@ -62,6 +62,10 @@ void orc_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc, co
 void orc_swiglu(const uint16_t* g, const uint16_t* u, int64_t n, uint16_t* out);
 void orc_residual_add(uint16_t* h, const uint16_t* y, int64_t n);
 int32_t orc_argmax(const uint16_t* logits, int64_t V);
+/* Seeded top-k / top-p sampling of one row against the uniform u (definition
+ * at the function); *margin (nullable) is the decisions' relative margin. */
+int32_t orc_sample(const uint16_t* logits, int64_t V, double temperature, int32_t top_k,
+                   double top_p, double u, double* margin);
 
 /* One block execution over `rows` rows at absolute positions pos[]: keys and
  * values of every row are stored at their slots first, then each row attends

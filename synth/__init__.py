@@ -37,6 +37,9 @@ def _load_host():
         lib.synth_tokens.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
                                      ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32]
         lib.synth_tokens.restype = None
+        lib.synth_uniform_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                          ctypes.c_uint64, ctypes.c_int64]
+        lib.synth_uniform_f32.restype = None
         _host = lib
     return _host
 
@@ -59,6 +62,9 @@ def _load_dev():
                                          ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32,
                                          ctypes.c_void_p]
         lib.synth_tokens_dev.restype = ctypes.c_int
+        lib.synth_uniform_f32_dev.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64,
+                                              ctypes.c_uint64, ctypes.c_int64, ctypes.c_void_p]
+        lib.synth_uniform_f32_dev.restype = ctypes.c_int
         _dev = lib
     return _dev
 
@@ -80,6 +86,14 @@ def tokens(n, seed, stream_id, vocab, offset=0):
     return out
 
 
+def uniform_f32(n, seed, stream_id, offset=0):
+    """Host float32 array of ``n`` values uniform over [0, 1) (24-bit)."""
+    out = np.empty(int(n), dtype=np.float32)
+    if n:
+        _load_host().synth_uniform_f32(out.ctypes.data, int(n), seed, stream_id, int(offset))
+    return out
+
+
 def normal_bf16_dev(ptr, n, seed, tensor_id, mean=0.0, std=1.0, offset=0, stream=0):
     """Fill ``n`` bf16 elements at device address ``ptr`` with the same bits as
     :func:`normal_bf16`.  Asynchronous on ``stream`` (a hipStream_t handle)."""
@@ -93,3 +107,9 @@ def tokens_dev(ptr, n, seed, stream_id, vocab, offset=0, stream=0):
     rc = _load_dev().synth_tokens_dev(ptr, int(n), seed, stream_id, int(offset), int(vocab), stream)
     if rc != 0:
         raise RuntimeError(f"synth_tokens_dev failed ({rc})")
+
+
+def uniform_f32_dev(ptr, n, seed, stream_id, offset=0, stream=0):
+    rc = _load_dev().synth_uniform_f32_dev(ptr, int(n), seed, stream_id, int(offset), stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_uniform_f32_dev failed ({rc})")

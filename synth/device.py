@@ -3,7 +3,7 @@ tensors), bit-identical to the host generator."""
 import numpy as np
 import torch
 
-from . import normal_bf16_dev, tokens_dev
+from . import normal_bf16_dev, tokens_dev, uniform_f32_dev
 from .workloads import weight_spec
 
 
@@ -31,6 +31,12 @@ def normal(shape, seed, tensor_id, mean=0.0, std=1.0, device="cuda", offset=0):
 def tokens(n, seed, stream_id, vocab, device="cuda", offset=0):
     t = torch.empty(int(n), dtype=torch.int32, device=device)
     tokens_dev(t.data_ptr(), int(n), seed, stream_id, vocab, offset=offset, stream=_stream())
+    return t
+
+
+def uniform(n, seed, stream_id, device="cuda", offset=0):
+    t = torch.empty(int(n), dtype=torch.float32, device=device)
+    uniform_f32_dev(t.data_ptr(), int(n), seed, stream_id, offset=offset, stream=_stream())
     return t
 
 

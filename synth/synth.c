@@ -16,3 +16,8 @@ void synth_tokens(int32_t* out, int64_t n, uint64_t seed, uint64_t tensor_id, in
   uint64_t key = synth_key(seed, tensor_id);
   for (int64_t i = 0; i < n; ++i) out[i] = synth_token_elem(key, (uint64_t)(offset + i), vocab);
 }
+
+void synth_uniform_f32(float* out, int64_t n, uint64_t seed, uint64_t tensor_id, int64_t offset) {
+  uint64_t key = synth_key(seed, tensor_id);
+  for (int64_t i = 0; i < n; ++i) out[i] = synth_uniform_elem(key, (uint64_t)(offset + i));
+}

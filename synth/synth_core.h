@@ -23,6 +23,8 @@
  *     host and device produce the same bits.
  *   - Uniform token ids in [0, V): the high 32 bits of output i, times V,
  *     shifted right by 32 (Lemire's multiply-shift range reduction).
+ *   - Uniform binary32 values in [0, 1): the high 24 bits of output i times
+ *     2^-24 (exact in binary32).
  */
 #ifndef SYNTH_CORE_H
 #define SYNTH_CORE_H
@@ -95,6 +97,10 @@ SYNTH_FN uint16_t synth_normal_elem(uint64_t key, uint64_t i, double mean, doubl
   double v = mean + p;
 #endif
   return synth_bf16(v);
+}
+
+SYNTH_FN float synth_uniform_elem(uint64_t key, uint64_t i) {
+  return (float)(uint32_t)(synth_draw(key, i) >> 40) * (1.0f / 16777216.0f);
 }
 
 SYNTH_FN int32_t synth_token_elem(uint64_t key, uint64_t i, int32_t vocab) {

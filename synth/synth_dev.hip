@@ -18,6 +18,12 @@ __global__ void synth_tokens_kernel(int32_t* out, int64_t n, uint64_t key, int64
     out[i] = synth_token_elem(key, (uint64_t)(offset + i), vocab);
 }
 
+__global__ void synth_uniform_kernel(float* out, int64_t n, uint64_t key, int64_t offset) {
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    out[i] = synth_uniform_elem(key, (uint64_t)(offset + i));
+}
+
 #include <stdio.h>
 
 // A launch failure is reported as -2 with its reason on stderr.  Errors left
@@ -54,4 +60,14 @@ extern "C" int synth_tokens_dev(void* out, int64_t n, uint64_t seed, uint64_t te
   hipLaunchKernelGGL(synth_tokens_kernel, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream,
                      (int32_t*)out, n, synth_key(seed, tensor_id), offset, vocab);
   return launched("synth_tokens_dev");
+}
+
+extern "C" int synth_uniform_f32_dev(void* out, int64_t n, uint64_t seed, uint64_t tensor_id,
+                                     int64_t offset, void* stream) {
+  if (n <= 0) return 0;
+  if (!out) return -1;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(synth_uniform_kernel, dim3(grid_for(n)), dim3(256), 0, (hipStream_t)stream,
+                     (float*)out, n, synth_key(seed, tensor_id), offset);
+  return launched("synth_uniform_f32_dev");
 }

@@ -96,6 +96,9 @@ class TensorIds:
     K_CACHE = 10
     V_CACHE = 11
     INPUT_ROWS = 20
+    # sampling: the uniform drawn for step s of a sequence, and synthetic logits
+    SAMPLE_UNIFORM = 30
+    SAMPLE_LOGITS = 31
 
     @staticmethod
     def block(b, kind):

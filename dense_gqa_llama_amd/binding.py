@@ -69,6 +69,8 @@ _SIGS = {
                                          ctypes.c_int32, _P, _P, _P, _P, _P]),
     "llama_set_capture": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "llama_check_finite": (ctypes.c_int, [_P, _P]),
+    "llama_sample": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                    ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
     "llama_set_timing": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32]),
     "llama_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(ctypes.c_int64)]),
@@ -184,6 +186,11 @@ def llama_set_capture(model, buf, nbytes):
 
 def llama_check_finite(model, stream=None):
     return _check(lib.llama_check_finite(model, stream))
+
+
+def llama_sample(model, logits_bf16, rows, ld, temperature, top_k, top_p, u, tokens, stream=None):
+    return _check(lib.llama_sample(model, logits_bf16, rows, ld, temperature, top_k, top_p, u,
+                                   tokens, stream))
 
 
 TIMING = {"off": 0, "gate_up": 1, "down": 2, "qkv": 3, "o": 4, "lm_head": 5, "attn": 6,

@@ -28,6 +28,13 @@ void launch_rope_table(const RowTable& tab, int rows, int d, float theta, void* 
 void launch_rope_kv(const void* qkv, void* qout, const RowTable& tab, int rows, int nq, int nkv,
                     int d, const void* table, hipStream_t s);
 int argmax_chunks(int V);
+// Seeded top-k / top-p sampling of bf16 logit rows (k <= 64); cv / ci / bad
+// hold rows * sample_chunks(V) * k candidates and rows * sample_chunks(V)
+// flags.
+int sample_chunks(int V);
+void launch_sample(const void* logits, int V, int64_t ld, int rows, int k, float temperature,
+                   float top_p, const float* u, float* cv, int* ci, int* bad, int32_t* out,
+                   int* flag, hipStream_t s);
 void launch_argmax(const void* logits, int V, int ld, int rows, float* pv, int* pi, int32_t* out,
                    int* flag, hipStream_t s);
 

@@ -32,7 +32,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Device workspace carved into fixed regions.
 struct Layout {
-  size_t h, x, qkv, q, att, m, rope, logits, amx_v, amx_i, part, flag, total;
+  size_t h, x, qkv, q, att, m, rope, logits, amx_v, amx_i, part, smp_v, smp_i, smp_bad, flag, total;
 };
 
 struct Dims {
@@ -80,6 +80,10 @@ Layout layout_of(const Dims& d) {
   L.amx_v = take((size_t)d.Llog * nch * 4);
   L.amx_i = take((size_t)d.Llog * nch * 4);
   L.part = take((size_t)d.Mdec * d.nq * attn_max_blocks() * (d.d + 2) * 4);
+  int nsc = d.V ? sample_chunks(d.V) : 1;
+  L.smp_v = take((size_t)LLAMA_SAMPLE_MAX_ROWS * nsc * LLAMA_SAMPLE_MAX_TOP_K * 4);
+  L.smp_i = take((size_t)LLAMA_SAMPLE_MAX_ROWS * nsc * LLAMA_SAMPLE_MAX_TOP_K * 4);
+  L.smp_bad = take((size_t)LLAMA_SAMPLE_MAX_ROWS * nsc * 4);
   L.flag = take(256);
   L.total = off;
   return L;
@@ -559,6 +563,32 @@ int llama_decode_step(llama_model* m, llama_kv* const* kvs, int32_t n_seq,
   return LLAMA_OK;
 }
 
+int llama_sample(llama_model* m, const void* logits_bf16_dev, int32_t rows, int64_t ld,
+                 float temperature, int32_t top_k, float top_p, const float* u_dev,
+                 int32_t* tokens_dev, void* hip_stream) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  const int V = m->d.V;
+  if (!V) return fail(LLAMA_E_ARG, "a blocks-only model has no logits to sample");
+  if (!logits_bf16_dev || !u_dev || !tokens_dev) return fail(LLAMA_E_ARG, "NULL buffer");
+  if (rows < 1 || rows > LLAMA_SAMPLE_MAX_ROWS)
+    return fail(LLAMA_E_ARG, "rows %d outside 1..%d", rows, LLAMA_SAMPLE_MAX_ROWS);
+  if (ld < V) return fail(LLAMA_E_ARG, "row stride %lld below the vocabulary %d", (long long)ld, V);
+  if (!(temperature > 0.0f) || !(temperature < INFINITY))
+    return fail(LLAMA_E_ARG, "temperature must be positive and finite (greedy draws take "
+                "next_tokens in the step calls)");
+  if (top_k < 1 || top_k > LLAMA_SAMPLE_MAX_TOP_K || top_k > V)
+    return fail(LLAMA_E_ARG, "top_k %d outside 1..%d", top_k, std::min(LLAMA_SAMPLE_MAX_TOP_K, V));
+  if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return fail(LLAMA_E_ARG, "top_p must lie in (0, 1]");
+  if (sample_chunks(V) * top_k > 4096)
+    return fail(LLAMA_E_ARG, "top_k %d too large for a vocabulary of %d", top_k, V);
+  hipStream_t s = (hipStream_t)hip_stream;
+  ready_flag(m, s);
+  launch_sample(logits_bf16_dev, V, ld, rows, top_k, temperature, top_p, u_dev,
+                m->at<float>(m->L.smp_v), m->at<int>(m->L.smp_i), m->at<int>(m->L.smp_bad),
+                tokens_dev, m->at<int>(m->L.flag), s);
+  return dev_check("sample launch");
+}
+
 int llama_check_finite(llama_model* m, void* hip_stream) {
   if (!m) return fail(LLAMA_E_ARG, "model is NULL");
   hipStream_t s = (hipStream_t)hip_stream;
@@ -570,7 +600,7 @@ int llama_check_finite(llama_model* m, void* hip_stream) {
   if (flag) {
     launch_fill_zero(m->at<int>(m->L.flag), 64, s);
     (void)hipStreamSynchronize(s);
-    return fail(LLAMA_E_NONFINITE, "a greedy draw met a logit row holding NaN or Inf");
+    return fail(LLAMA_E_NONFINITE, "a greedy or sampled draw met a logit row holding NaN or Inf");
   }
   return LLAMA_OK;
 }

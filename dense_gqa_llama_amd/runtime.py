@@ -99,6 +99,17 @@ class Model:
                             _ptr(out.get("logits32")), _ptr(out.get("next")), _stream())
         return out
 
+    def sample(self, logits, u, temperature, top_k, top_p, out=None):
+        """Seeded top-k / top-p draw for each row of ``logits`` (bf16 bits as
+        int16 [rows][>= vocab]) against the uniforms ``u`` (float32 [rows]);
+        returns int32 token ids (-1 for a non-finite row)."""
+        rows = logits.shape[0]
+        if out is None:
+            out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+        B.llama_sample(self.handle, logits.data_ptr(), rows, logits.stride(0), float(temperature),
+                       int(top_k), float(top_p), u.data_ptr(), out.data_ptr(), _stream())
+        return out
+
     def check_finite(self):
         B.llama_check_finite(self.handle, _stream())
 

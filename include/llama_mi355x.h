@@ -178,9 +178,35 @@ enum {
 int llama_set_timing(llama_model* model, int32_t kernel, int32_t max_launches);
 int llama_timing_read(llama_model* model, double* total_ms, int64_t* launches);
 
-/* Synchronises hip_stream, then reports LLAMA_E_NONFINITE if any greedy
- * draw since the last call met a non-finite logit row (and clears the
- * flag), else LLAMA_OK. */
+/* Seeded sampling (issue "A llama family on Metal", the served sampling
+ * checks; pull request, section "How": tokens drawn on the GPU; model card
+ * "Nanbeige4.3-33B EXL3": upstream's recommended temperature 0.6, top_p 0.95,
+ * top_k 20).  For each of `rows` rows of bf16 logits (row r at
+ * logits_bf16_dev + r * ld elements, `vocab` entries, e.g. the logits a step
+ * call wrote) it draws one token into tokens_dev[r] (int32, device):
+ *   z = logit / temperature; keep the top_k largest (ties to the lower id),
+ *   ordered largest first; weights e_i = exp(z_i - z_0); candidate i stays
+ *   while the weight of those before it is below top_p times the total (the
+ *   first always stays); the token is the first remaining candidate whose
+ *   running weight exceeds u_dev[r] times the remaining weight.
+ * u_dev holds one uniform in [0, 1) per row (float, device), drawn by the
+ * caller from its seed, so equal seeds give equal tokens.  Weights and draw
+ * are fp32.  rows 1..LLAMA_SAMPLE_MAX_ROWS; temperature > 0 and finite (a
+ * greedy draw is the step calls' next_tokens); top_k 1..LLAMA_SAMPLE_MAX_TOP_K
+ * (and at most vocab); 0 < top_p <= 1.  A row holding NaN or +-Inf yields -1
+ * and raises the non-finite flag (llama_check_finite).  Refusals return
+ * LLAMA_E_ARG before anything is enqueued.  Asynchronous on hip_stream; uses
+ * the model's workspace, so calls on one model are serialised by its
+ * stream. */
+#define LLAMA_SAMPLE_MAX_ROWS 64
+#define LLAMA_SAMPLE_MAX_TOP_K 64
+int llama_sample(llama_model* model, const void* logits_bf16_dev, int32_t rows, int64_t ld,
+                 float temperature, int32_t top_k, float top_p, const float* u_dev,
+                 int32_t* tokens_dev, void* hip_stream);
+
+/* Synchronises hip_stream, then reports LLAMA_E_NONFINITE if any greedy or
+ * sampled draw since the last call met a non-finite logit row (and clears
+ * the flag), else LLAMA_OK. */
 int llama_check_finite(llama_model* model, void* hip_stream);
 
 void llama_kv_free(llama_kv* kv);

@@ -156,3 +156,31 @@ def test_blocks_only_model_refuses_tokens_and_logits():
         B.llama_kv_free(kv)
     finally:
         B.llama_free(m)
+
+
+def test_sampling_refusals():
+    g = CONFIGS[1]
+    m, cfg = load(g, max_chunk_rows=64)
+    try:
+        V = g.vocab
+        ok = dict(rows=4, ld=V, temperature=0.6, top_k=20, top_p=0.95)
+
+        def call(**kw):
+            a = dict(ok)
+            a.update(kw)
+            return B.llama_sample(m, kw.get("logits", FAKE), a["rows"], a["ld"], a["temperature"],
+                                  a["top_k"], a["top_p"], kw.get("u", FAKE), kw.get("tok", FAKE))
+        for kw in (dict(rows=0), dict(rows=65), dict(ld=V - 1), dict(temperature=0.0),
+                   dict(temperature=-1.0), dict(temperature=float("inf")),
+                   dict(temperature=float("nan")), dict(top_k=0), dict(top_k=65),
+                   dict(top_p=0.0), dict(top_p=1.5), dict(top_p=float("nan")),
+                   dict(logits=None), dict(u=None), dict(tok=None)):
+            expect(B.LLAMA_E_ARG, call, **kw)
+    finally:
+        B.llama_free(m)
+    g2 = CONFIGS[2]
+    m2, _ = load(g2, max_chunk_rows=16)
+    try:
+        expect(B.LLAMA_E_ARG, B.llama_sample, m2, FAKE, 1, 128, 1.0, 1, 1.0, FAKE, FAKE)
+    finally:
+        B.llama_free(m2)

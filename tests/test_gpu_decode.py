@@ -42,6 +42,9 @@ def test_device_generator_matches_host():
     assert (u16(t) == synth.normal_bf16(4096, 1003, 2, 1.0, 0.02, offset=123456)).all()
     tk = sd.tokens(5000, 2003, 0, 166912)
     assert (tk.cpu().numpy() == synth.tokens(5000, 2003, 0, 166912)).all()
+    un = sd.uniform(5000, 4401, TensorIds.SAMPLE_UNIFORM, offset=77)
+    assert (un.cpu().numpy() == synth.uniform_f32(5000, 4401, TensorIds.SAMPLE_UNIFORM,
+                                                  offset=77)).all()
 
 
 # ----------------------------------------------------------------- tiny ----

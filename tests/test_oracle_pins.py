@@ -384,3 +384,14 @@ def test_embed_gathers_rows():
     E = rand_bf16((10, 8))
     out = oracle.embed(E, [3, 0, 9, 3])
     assert (out == E[[3, 0, 9, 3]]).all()
+
+
+def test_uniform_generator_range_and_moments():
+    """The shared 24-bit uniform generator: values k * 2^-24 in [0, 1), mean
+    1/2 and variance 1/12 to within sampling error, independent of offset."""
+    import synth
+    u = synth.uniform_f32(200000, 4500, 30)
+    assert u.min() >= 0.0 and u.max() < 1.0
+    assert np.all(u * 16777216.0 == np.floor(u * 16777216.0))
+    assert abs(u.mean() - 0.5) < 0.005 and abs(u.var() - 1.0 / 12) < 0.002
+    assert np.array_equal(synth.uniform_f32(100, 4500, 30, offset=1000), u[1000:1100])

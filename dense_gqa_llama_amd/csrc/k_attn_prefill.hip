@@ -26,7 +26,15 @@ namespace {
 
 constexpr int QT = 128;  // chunk rows per workgroup
 constexpr int KT = 64;   // cache slots per LDS tile
-constexpr int VPAD = 4;
+constexpr int VPAD = 8;  // V^T rows of 144 B: 16-byte fragment reads are conflict-free
+
+// Column of tile slot s in the transposed value tile.  Within each 16-slot
+// step the slots are stored in the order the PV product's k slots take them
+// (lane half h reads k slots 8h .. 8h + 7 = keys 4h .. 4h + 3, 8 + 4h .. 11 +
+// 4h): slots 0-3, 8-11, 4-7, 12-15, so a fragment is one 16-byte read.
+__device__ __forceinline__ int vcol(int s) {
+  return (s & ~15) | ((s >> 2) & 1) << 3 | ((s >> 3) & 1) << 2 | (s & 3);
+}
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
@@ -50,11 +58,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
   constexpr int KCH = KT * D / 8 / 256;   // 16-byte key chunks per thread per tile
   constexpr int DCH = D / 8;              // 16-byte chunks per slot
   constexpr int VS = KT * DCH / 256;      // value slots per thread per tile
+  constexpr int NGRP = KT / VS;           // value slot groups per tile
   static_assert(VS == 2 || VS == 4, "value staging takes 2 or 4 slots per thread");
+  static_assert(NGRP * DCH == 256 && NGRP <= 32, "value staging covers the tile");
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * KLD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][D * VLD];
-  __shared__ int sBad[2][KT];   // slot holds a non-finite value
-  __shared__ int sBadW[2][4];   // some slot of the tile does (per staging wave)
+  __shared__ uint32_t sBadM[2][4][VS];  // per staging wave and slot j of a group: group bits
+  __shared__ int sBadW[2][4];           // some slot of the tile is flagged (per staging wave)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // heaviest row blocks first: block x covers rows of block (nblk - 1 - x)
@@ -78,9 +88,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
     for (int t = 0; t < D / 16; ++t) qf[t] = *(const bf16x8_t*)(src + 16 * t);
   }
 
-  // staging: keys as KCH chunks (slot c/DCH, dims (c%DCH)*8), values as VS
-  // consecutive slots VS*(tid/DCH) .. at dims (tid%DCH)*8
-  const int vslot = VS * (tid / DCH), vdc = (tid % DCH) * 8;
+  // staging: keys as KCH chunks (slot c/DCH, dims (c%DCH)*8); values as a
+  // group of VS consecutive slots VS*(tid%NGRP) .. at dims 8*(tid/NGRP), so
+  // the 16 lanes of an LDS write fill one transposed row
+  const int vslot = VS * (tid % NGRP), vdc = 8 * (tid / NGRP);
   u32x4_t rk[KCH], rv[VS];
   // Slots past the block's last query are masked for every row of the block;
   // their loads are clamped to that last slot (a valid cache row).
@@ -96,12 +107,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
       rv[j] = *(const u32x4_t*)(vc + (size_t)p * kvd + g * D + vdc);
     }
   };
-  // Values are staged transposed.  A masked slot still meets a zero weight in
-  // the value product, and 0 * NaN would leak into earlier rows, so
-  // non-finite values are staged as zero and their slot flagged: a score
-  // against a flagged slot that is not masked becomes NaN, which is what the
-  // rows attending to it would get.
-  auto lstore = [&](int buf) {
+  // Values are staged transposed.  On a tile where some row of the block has
+  // masked slots, a masked slot still meets a zero weight in the value
+  // product, and 0 * NaN would leak into earlier rows, so non-finite values
+  // are staged as zero there and their slot flagged: a score against a
+  // flagged slot that is not masked becomes NaN, which is what the rows
+  // attending to it get.  On the other tiles every row attends to every slot
+  // and a non-finite value reaches every row through the product itself.
+  const int block_first = pos0 + r0;
+  auto lstore = [&](int buf, int k0) {
+    const bool masked = k0 + KT - 1 > block_first;  // uniform per workgroup
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int c = tid + i * 256;
@@ -111,7 +126,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
     uint32_t any = 0;
 #pragma unroll
     for (int j = 0; j < VS; ++j) {
-      badj[j] = nonfinite2(rv[j].x) | nonfinite2(rv[j].y) | nonfinite2(rv[j].z) | nonfinite2(rv[j].w);
+      badj[j] = masked ? nonfinite2(rv[j].x) | nonfinite2(rv[j].y) | nonfinite2(rv[j].z) |
+                             nonfinite2(rv[j].w)
+                       : 0u;
       any |= badj[j];
     }
     if (any) {  // rare: zero the non-finite halves
@@ -135,20 +152,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
       if (VS == 4) {
         const uint32_t w2 = rv[VS > 2 ? 2 : 0][e], w3 = rv[VS > 2 ? 3 : 0][e];
         const uint32_t lo23 = (w2 & 0xFFFFu) | (w3 << 16), hi23 = (w2 >> 16) | (w3 & 0xFFFF0000u);
-        *(uint2*)&sV[buf][(vdc + 2 * e) * VLD + vslot] = make_uint2(lo01, lo23);
-        *(uint2*)&sV[buf][(vdc + 2 * e + 1) * VLD + vslot] = make_uint2(hi01, hi23);
+        *(uint2*)&sV[buf][(vdc + 2 * e) * VLD + vcol(vslot)] = make_uint2(lo01, lo23);
+        *(uint2*)&sV[buf][(vdc + 2 * e + 1) * VLD + vcol(vslot)] = make_uint2(hi01, hi23);
       } else {
-        *(uint32_t*)&sV[buf][(vdc + 2 * e) * VLD + vslot] = lo01;
-        *(uint32_t*)&sV[buf][(vdc + 2 * e + 1) * VLD + vslot] = hi01;
+        *(uint32_t*)&sV[buf][(vdc + 2 * e) * VLD + vcol(vslot)] = lo01;
+        *(uint32_t*)&sV[buf][(vdc + 2 * e + 1) * VLD + vcol(vslot)] = hi01;
       }
     }
-    // a slot's flag is the OR over the DCH threads holding its dims
+    if (!masked) {  // nothing zeroed, nothing flagged
+      if (lane == 0) sBadW[buf][wave] = 0;
+      return;
+    }
+    // per wave and slot j of a group: the groups holding a flagged value
+    // in this wave's dims (lanes l, l + NGRP, ... share a group)
 #pragma unroll
     for (int j = 0; j < VS; ++j) {
       uint32_t f = badj[j];
 #pragma unroll
-      for (int m = 1; m < DCH; m <<= 1) f |= __shfl_xor(f, m, WAVE);
-      if (vdc == 0) sBad[buf][vslot + j] = f != 0;
+      for (int m = NGRP; m < WAVE; m <<= 1) f |= __shfl_xor(f, m, WAVE);
+      const uint64_t b = __ballot(f != 0);
+      if (lane == 0) sBadM[buf][wave][j] = (uint32_t)b & (uint32_t)((1ull << NGRP) - 1);
     }
     const int wany = __any(any != 0);
     if (lane == 0) sBadW[buf][wave] = wany;
@@ -163,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
 
   const int ntiles = block_last / KT + 1;
   gload(0);
-  lstore(0);
+  lstore(0, 0);
   __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * KT, buf = kt & 1;
@@ -172,31 +195,41 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
       // S^T = K Q^T for 64 keys (two 32-key halves) x 32 queries
       f32x16_t s[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[u][r] = 0.f;
+      // the two halves' products interleave (independent accumulators)
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          bf16x8_t kf = *(const bf16x8_t*)&sK[buf][(32 * u + lq) * KLD + 16 * t + 8 * half];
+      for (int t = 0; t < D / 16; ++t) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8_t kf = *(const bf16x8_t*)&sK[buf][(32 * u + lq) * KLD + 16 * t + 8 * half];
           s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[u], 0, 0, 0);
         }
       }
       // keys of register r of half u: k0 + 32u + 8*(r/4) + 4*half + r%4
-      const bool any_bad = sBadW[buf][0] | sBadW[buf][1] | sBadW[buf][2] | sBadW[buf][3];
+      // (raw scores here; the scale enters the exponent below)
       const bool diag = k0 + KT - 1 > wave_first;
+      const bool any_bad = sBadW[buf][0] | sBadW[buf][1] | sBadW[buf][2] | sBadW[buf][3];
+      if (any_bad) {  // rare: zeroed non-finite values (flag reads kept off the common path)
+        const volatile uint32_t* bm = &sBadM[buf][0][0];
+        uint32_t gm[VS];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[u][r] *= c2;
-      if (any_bad | diag) {  // tiles on the diagonal, or holding a non-finite value
+        for (int j = 0; j < VS; ++j) gm[j] = bm[j] | bm[VS + j] | bm[2 * VS + j] | bm[3 * VS + j];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ko = 32 * u + 8 * (r >> 2) + 4 * half + (r & 3);
-            float v = sBad[buf][ko] ? NAN : s[u][r];
-            s[u][r] = k0 + ko > qpos ? -INFINITY : v;
+            if (gm[ko % VS] >> (ko / VS) & 1u) s[u][r] = NAN;
           }
+      }
+      if (diag) {  // tiles reaching past the wave's first query
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (k0 + 32 * u + 8 * (r >> 2) + 4 * half + (r & 3) > qpos) s[u][r] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -205,9 +238,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
       const float mnew = fmaxf(mrow, mx);
-      // a row with no unmasked key yet keeps zero weights
+      // weights exp2(c2 * (s - m)) with c2 = log2(e)/sqrt(d), as one
+      // multiply-add per score; a row with no unmasked key yet keeps zero
+      // weights.  The rescale factor is exactly 1 while the maximum holds (a
+      // tile all of whose keys are masked for a row leaves its sums alone, so
+      // a row's bits never depend on which other rows share its chunk).
       const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(mrow - mref);
+      const float moff = -mref * c2;
+      const float alpha = __builtin_amdgcn_exp2f((mrow - mref) * c2);
       mrow = mnew;
       if (!__all(alpha == 1.f)) {
 #pragma unroll
@@ -224,8 +262,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
         uint32_t pk[4], pl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + 2 * i] - mref);
-          const float p1 = __builtin_amdgcn_exp2f(s[st >> 1][8 * (st & 1) + 2 * i + 1] - mref);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + 2 * i], c2, moff));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + 2 * i + 1], c2, moff));
           psum += p0;
           psum += p1;
           const uint32_t hw = cvt_pk_bf16(p0, p1);
@@ -234,19 +272,23 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
         }
         const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
         const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, u32x4_t{pl[0], pl[1], pl[2], pl[3]});
+        bf16x8_t vf[D / 32];
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
-          const bf16_t* vrow = &sV[buf][(i * 32 + lq) * VLD + 16 * st + 4 * half];
-          const uint2 lo = *(const uint2*)vrow, hi = *(const uint2*)(vrow + 8);
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfl, acc[i], 0, 0, 0);
-        }
+        for (int i = 0; i < D / 32; ++i)
+          vf[i] = *(const bf16x8_t*)&sV[buf][(i * 32 + lq) * VLD + 16 * st + 8 * half];
+        // hi parts over all accumulators, then lo parts: no back-to-back
+        // dependent products
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pf, acc[i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pfl, acc[i], 0, 0, 0);
       }
       psum += __shfl_xor(psum, 32, WAVE);
       lrow = lrow * alpha + psum;
     }
-    if (kt + 1 < ntiles) lstore(buf ^ 1);
+    if (kt + 1 < ntiles) lstore(buf ^ 1, k0 + KT);
     __syncthreads();
   }
 

@@ -29,7 +29,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # the sources they were taken on (a changed kernel reports no traffic)
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemv_gate_up_33b_decode_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "dense_gqa_llama_amd", "csrc", f)
-                  for f in ("k_gemv.hip", "common.h", "launch.h")]
+                  for f in ("k_gemv.hip", "common.h")]
 
 
 def log(msg):

@@ -24,6 +24,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+STREAMS = (2, 12)      # concurrent sequences sharing every decode round
+STREAM_ROUNDS = 32
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes of the dominant kernel from rocprofv3 counters, with the digest of
 # the sources they were taken on (a changed kernel reports no traffic)
@@ -180,7 +182,8 @@ def main():
     log(f"generating {g.params() * 2 / 2**30:.2f} GiB of weights on the GPU")
     w = sd.weights(g)
     torch.cuda.synchronize()
-    model = L.Model(g, w, max_positions=cap, max_chunk_rows=P, max_window_rows=16, max_seqs=2)
+    model = L.Model(g, w, max_positions=cap, max_chunk_rows=P, max_window_rows=16,
+                    max_seqs=STREAMS[-1])
     seq = model.new_sequence(cap)
     prompt = sd.tokens(P, g.prompt_seeds[0], 0, g.vocab)
     stream = torch.cuda.current_stream()
@@ -251,6 +254,44 @@ def main():
         f"{attn_ms:.1f} ms ({attn_tf:.0f} TFLOP/s)")
     traffic = stored_traffic()
 
+    # concurrent streams: n sequences, each with the prompt, share every decode
+    # round (one row per sequence); aggregate tokens per second
+    streams = [{"n": 1, "tok_s": round(dec_tps, 2)}]
+    for n in STREAMS:
+        seqs = [model.new_sequence(P + STREAM_ROUNDS + 1) for _ in range(n)]
+        firsts = [model.prefill(sq, tokens=prompt, want_logits=False)["next"] for sq in seqs]
+        tok = torch.cat(firsts)
+        model.decode(seqs, tokens=tok, want_logits=False, next_out=tok)  # warm
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(STREAM_ROUNDS):
+            model.decode(seqs, tokens=tok, want_logits=False, next_out=tok)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        streams.append({"n": n, "tok_s": round(n * STREAM_ROUNDS / (ms / 1e3), 2)})
+        log(f"{n} streams: {streams[-1]['tok_s']:.1f} tok/s together ({ms / STREAM_ROUNDS:.2f} ms a round)")
+        del seqs
+    torch.cuda.empty_cache()
+
+    # seeded sampling of one logit row (temperature 0.6, top_k 20, top_p 0.95)
+    sq = model.new_sequence(cap)
+    lg = model.prefill(sq, tokens=prompt)["logits"]
+    u = sd.uniform(256, 4600, 30)
+    out = torch.empty(1, dtype=torch.int32, device="cuda")
+    model.sample(lg, u[:1], 0.6, 20, 0.95, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(256):
+        model.sample(lg, u[i:i + 1], 0.6, 20, 0.95, out=out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    sample_us = a.elapsed_time(b) * 1e3 / 256
+    log(f"sampling: {sample_us:.1f} us per row")
+    del sq
+
     result = {
         "metric": "decode tok/s + HBM GB/s (% peak), 33B bf16 batch 1; prefill tok/s",
         "value": round(dec_tps, 3),
@@ -281,6 +322,9 @@ def main():
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                               "ms_per_chunk": round(attn_ms, 3)},
+        "streams": streams,
+        "sampling": {"us_per_row": round(sample_us, 2), "temperature": 0.6, "top_k": 20,
+                     "top_p": 0.95},
         "roofline": {"bound": "hbm", "kernel": "decode gate/up projection + SwiGLU (R=1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -254,11 +254,26 @@ void launch_tile(const GemmArgs& a, int ncols, hipStream_t s) {
 
 }  // namespace
 
+// Compute units of the current device (tiles are handed out in rounds of
+// one workgroup per CU).
+static int cu_count() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+  }
+  return n;
+}
+
 // ncols: tile columns (N, or 2F for SWIGLU); a multiple of 128.  Widths that
 // are multiples of 256 take 256 x 256 tiles (eight waves of 128 x 64), which
-// halve the LDS and L2 traffic per product of the 128 x 128 tiles; the split
-// of K into 16-deep MFMA steps, and so every output's bits, is the same for
-// both.
+// halve the LDS and L2 traffic per product of the 128 x 128 tiles; when the
+// 256-wide tiles would leave the last round of workgroups mostly empty, 256 x
+// 128 tiles (eight waves of 64 x 64, about 15% slower per product) fill the
+// CUs better.  The split of K into 64-deep tiles and 16-deep MFMA steps, and so
+// every output's bits, is the same for all of them.
 void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* seg, int nseg,
                  const void* gate, const void* up, void* out, int ldo, float* out32, int ld32,
                  int ncols, hipStream_t s) {
@@ -276,14 +291,24 @@ void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* s
   a.out32 = out32;
   a.ld32 = ld32;
   const bool big = ncols % 256 == 0;
+  bool narrow = false;
+  if (big) {
+    const int cus = cu_count(), mt = (M + 255) / 256;
+    const int rounds256 = ((ncols / 256) * mt + cus - 1) / cus;
+    const int rounds128 = ((ncols / 128) * mt + cus - 1) / cus;
+    narrow = rounds128 * 0.575 < rounds256 * 1.0;
+  }
   if (epi == GEMV_STORE) {
-    if (big) launch_tile<256, 256, 128, 64, GEMV_STORE>(a, ncols, s);
+    if (narrow) launch_tile<256, 128, 64, 64, GEMV_STORE>(a, ncols, s);
+    else if (big) launch_tile<256, 256, 128, 64, GEMV_STORE>(a, ncols, s);
     else launch_tile<128, 128, 64, 64, GEMV_STORE>(a, ncols, s);
   } else if (epi == GEMV_RESIDUAL) {
-    if (big) launch_tile<256, 256, 128, 64, GEMV_RESIDUAL>(a, ncols, s);
+    if (narrow) launch_tile<256, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
+    else if (big) launch_tile<256, 256, 128, 64, GEMV_RESIDUAL>(a, ncols, s);
     else launch_tile<128, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
   } else {
-    if (big) launch_tile<256, 256, 128, 64, GEMV_SWIGLU>(a, ncols, s);
+    if (narrow) launch_tile<256, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
+    else if (big) launch_tile<256, 256, 128, 64, GEMV_SWIGLU>(a, ncols, s);
     else launch_tile<128, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
   }
 }

@@ -60,6 +60,23 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 // rows itself, so a row's bits never depend on which of the two ran: a full
 // wave sums the row, lane l taking 16-byte vectors l, l+64, ... in order with
 // fused multiply-adds, then the xor butterfly.  H is a multiple of 8.
+// One 16-byte vector's squares added to a running sum, elements in order.
+__device__ __forceinline__ float sumsq8(u32x4_t q, float ss) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float a = bf_lo(w[j]), b = bf_hi(w[j]);
+    ss = fmaf(a, a, ss);
+    ss = fmaf(b, b, ss);
+  }
+  return ss;
+}
+
+__device__ __forceinline__ float inv_rms(float lane_ss, int H, float eps) {
+  const float ss = wave_sum(lane_ss);
+  return 1.0f / sqrtf(ss / (float)H + eps);
+}
+
 __device__ __forceinline__ float row_inv_rms(const bf16_t* __restrict__ x, int H, float eps) {
   const u32x4_t* xv = (const u32x4_t*)x;
   const int nv = H / 8;
@@ -75,17 +92,18 @@ __device__ __forceinline__ float row_inv_rms(const bf16_t* __restrict__ x, int H
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (v0 + i * WAVE >= nv) break;
-      const uint32_t w[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = bf_lo(w[j]), b = bf_hi(w[j]);
-        ss = fmaf(a, a, ss);
-        ss = fmaf(b, b, ss);
-      }
+      ss = sumsq8(q[i], ss);
     }
   }
-  ss = wave_sum(ss);
-  return 1.0f / sqrtf(ss / (float)H + eps);
+  return inv_rms(ss, H, eps);
+}
+
+// The same sum over a row already staged in LDS (nv = H / 8 vectors).
+__device__ __forceinline__ float row_inv_rms_lds(const u32x4_t* xv, int H, float eps) {
+  const int nv = H / 8;
+  float ss = 0.f;
+  for (int v = lane_id(); v < nv; v += WAVE) ss = sumsq8(xv[v], ss);
+  return inv_rms(ss, H, eps);
 }
 
 // Eight normalised elements: bf16(w * bf16(x * r)), packed.

@@ -35,15 +35,18 @@ struct GemvArgs {
   // NORM: the input rows are raw residuals, normalised here with this weight
   const bf16_t* normw;
   float eps;
+  // 16-byte vectors per row of each chunk of the input rows staged in LDS (a
+  // multiple of the loop step, or at least K/8: one chunk)
+  int xcv;
 };
 
 __device__ __forceinline__ float silu_bf16(float g) { return rbf(g / (1.0f + expf(-g))); }
 
 // NR weight rows per wave; for SWIGLU the first NR/2 come from the gate
 // matrix and the last NR/2 from the up matrix, for the same output columns.
-template <int R, int NR, int EPI, bool NORM, bool XLDS, int P>
+template <int R, int NR, int EPI, bool NORM, int P>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
-  extern __shared__ u32x4_t sx[];  // XLDS: the (normalised) input rows, [R][K/8]
+  extern __shared__ u32x4_t sx[];  // a chunk of the (normalised) input rows, [R][xcv]
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
   static_assert(EPI != GEMV_QKV_ROPE || NR == 4, "rotation pairs come four rows per wave");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -94,61 +97,101 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int xs = a.ldx >> 3;
   // Software pipeline, P steps deep: the weight vectors of the next P steps
   // are in flight while this step's are consumed; the first loads are issued
-  // before the norm prologue so its row reads overlap them.  The partial sums
-  // still take the vectors v = lane, lane + 64, ... in order.
+  // before the input rows are staged, so the staging overlaps them.  Every
+  // load is issued unconditionally (past the end a lane re-reads the row's
+  // last vector), so the loads in flight never depend on the lane and the
+  // waits stay exact.  The partial sums still take the vectors v = lane,
+  // lane + 64, ... in order.
   u32x4_t wq[P][NR];
 #pragma unroll
-  for (int p = 0; p < P; ++p)
-    if (lane + p * WAVE < nv) {
+  for (int p = 0; p < P; ++p) {
+    const int v = min(lane + p * WAVE, nv - 1);
 #pragma unroll
-      for (int i = 0; i < NR; ++i) wq[p][i] = GEMV_WLOAD(wp[i] + lane + p * WAVE);
-    }
-  float rs[R];
-  if (NORM) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) rs[r] = row_inv_rms(a.x + (size_t)r * a.ldx, a.K, a.eps);
+    for (int i = 0; i < NR; ++i) wq[p][i] = GEMV_WLOAD(wp[i] + v);
   }
+  // The input rows are staged in LDS a chunk of xcv vectors at a time, the
+  // whole rows when they fit: every wave walks the same steps, so the chunk
+  // boundaries and their barriers are uniform.  With NORM and whole rows the
+  // norm factors are summed from LDS and the rows normalised in place; with
+  // chunks, wave r first sums row r from memory and each chunk is normalised
+  // as it is staged.  Both sums take the canonical order.
+  __shared__ float srs[NORM ? R : 1];
   const u32x4_t* nw = (const u32x4_t*)a.normw;
-  if (XLDS) {
-    for (int i = threadIdx.x; i < R * nv; i += blockDim.x) {
-      const int r = i / nv, v = i - r * nv;
-      u32x4_t xv = xb[r * xs + v];
-      if (NORM) xv = norm8(xv, nw[v], rs[r]);
-      sx[i] = xv;
+  const int cv = a.xcv;
+  const bool whole = cv >= nv;
+  if (NORM && !whole) {
+    if (wave < R) {
+      const float rs = row_inv_rms(a.x + (size_t)wave * a.ldx, a.K, a.eps);
+      if (lane == 0) srs[wave] = rs;
     }
     __syncthreads();
   }
-  for (int v0 = lane; v0 < nv; v0 += P * WAVE) {
+  int c0 = 0;
+  for (int base = 0; base < nv; base += P * WAVE) {
+    if (base % cv == 0) {
+      if (base) __syncthreads();  // the previous chunk's readers are done
+      const int cn = min(cv, nv - base), tot = R * cn;
+      // XU vectors per thread and pass; past the end a thread repeats the
+      // last vector (the same value to the same slot)
+      constexpr int XU = NORM ? 2 : 4;
+      for (int i0 = threadIdx.x; i0 < tot; i0 += XU * 256) {
+        u32x4_t t[XU], g[XU];
+        int o[XU], rr[XU];
+#pragma unroll
+        for (int j = 0; j < XU; ++j) {
+          const int i = min(i0 + 256 * j, tot - 1);
+          const int r = i / cn, vv = i - r * cn;
+          t[j] = xb[r * xs + base + vv];
+          if (NORM && !whole) g[j] = nw[base + vv];
+          o[j] = r * cv + vv;
+          rr[j] = r;
+        }
+#pragma unroll
+        for (int j = 0; j < XU; ++j) sx[o[j]] = NORM && !whole ? norm8(t[j], g[j], srs[rr[j]]) : t[j];
+      }
+      __syncthreads();
+      if (NORM && whole) {
+        if (wave < R) {
+          const float rs = row_inv_rms_lds(sx + wave * cv, a.K, a.eps);
+          if (lane == 0) srs[wave] = rs;
+        }
+        __syncthreads();
+        for (int i0 = threadIdx.x; i0 < tot; i0 += 4 * 256) {
+          u32x4_t g[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) g[j] = nw[min(i0 + 256 * j, tot - 1) % cn];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = i0 + 256 * j;
+            if (i < tot) sx[i] = norm8(sx[i], g[j], srs[i / cn]);
+          }
+        }
+        __syncthreads();
+      }
+      c0 = base;
+    }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const int v = v0 + p * WAVE;
-      if (v >= nv) break;
+      const int v = base + p * WAVE + lane;
       u32x4_t w[NR];
 #pragma unroll
       for (int i = 0; i < NR; ++i) w[i] = wq[p][i];
-      if (v + P * WAVE < nv) {
+      const int vn = min(v + P * WAVE, nv - 1);
 #pragma unroll
-        for (int i = 0; i < NR; ++i) wq[p][i] = GEMV_WLOAD(wp[i] + v + P * WAVE);
-      }
-      u32x4_t g;
-      if (NORM && !XLDS) g = nw[v];
+      for (int i = 0; i < NR; ++i) wq[p][i] = GEMV_WLOAD(wp[i] + vn);
+      if (v < nv) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        u32x4_t xv;
-        if (XLDS) {
-          xv = sx[r * nv + v];
-        } else {
-          xv = xb[r * xs + v];
-          if (NORM) xv = norm8(xv, g, rs[r]);
-        }
+        for (int r = 0; r < R; ++r) {
+          const u32x4_t xv = sx[r * cv + (v - c0)];
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-          float t = acc[i][r];
-          t = dot2(w[i].x, xv.x, t);
-          t = dot2(w[i].y, xv.y, t);
-          t = dot2(w[i].z, xv.z, t);
-          t = dot2(w[i].w, xv.w, t);
-          acc[i][r] = t;
+          for (int i = 0; i < NR; ++i) {
+            float t = acc[i][r];
+            t = dot2(w[i].x, xv.x, t);
+            t = dot2(w[i].y, xv.y, t);
+            t = dot2(w[i].z, xv.z, t);
+            t = dot2(w[i].w, xv.w, t);
+            acc[i][r] = t;
+          }
         }
       }
     }
@@ -210,24 +253,35 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
 }
 
-// Input rows are staged in LDS when they fit in this many bytes.
+// Input rows staged in LDS: whole rows for one-row steps up to 64 KB, for
+// normalised windows up to GEMV_NORM_WHOLE_BYTES; otherwise chunks of at most
+// 32 KB (a multiple of the loop step).
 constexpr int GEMV_XLDS_BYTES = 64 * 1024;
+constexpr int GEMV_XCHUNK_BYTES = 32 * 1024;
+#ifndef GEMV_NORM_WHOLE_BYTES
+#define GEMV_NORM_WHOLE_BYTES (32 * 1024)
+#endif
 
 template <int R, int EPI, bool NORM>
-static void launch_r(const GemvArgs& a, int N, hipStream_t s) {
-  // weight rows per wave: more for small windows (more bytes in flight per
-  // wave), fewer for large ones (register budget of the R*NR partials); the
-  // prefetch depth shrinks with the window for the same reason.
-  constexpr int NR = EPI == GEMV_QKV_ROPE ? 4
-                     : EPI == GEMV_SWIGLU ? (R <= 4 ? 4 : 2) : (R <= 2 ? 4 : 2);
-  constexpr int P = R == 1 ? 4 : R <= 4 ? 2 : 1;
+static void launch_r(GemvArgs a, int N, hipStream_t s) {
+  // Four weight rows per wave; the prefetch depth is four steps for one-row
+  // steps and two for windows (register budget of the R*4 partials).
+  constexpr int NR = 4;
+  constexpr int P = R == 1 ? 4 : 2;
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
-  int grid = N / (4 * COLS);
-  const size_t xbytes = (size_t)R * a.K * 2;
-  if (xbytes <= GEMV_XLDS_BYTES)
-    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, true, P>), dim3(grid), dim3(256), xbytes, s, a);
-  else
-    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, false, P>), dim3(grid), dim3(256), 0, s, a);
+  const int grid = N / (4 * COLS);
+  const int nv = a.K / 8;
+  int cv;
+  const size_t rows_bytes = (size_t)R * a.K * 2;
+  if ((R == 1 && rows_bytes <= GEMV_XLDS_BYTES) || (NORM && rows_bytes <= GEMV_NORM_WHOLE_BYTES)) {
+    cv = nv;
+  } else {
+    cv = GEMV_XCHUNK_BYTES / (16 * R) / (P * WAVE) * (P * WAVE);
+    if (cv >= nv) cv = nv;
+  }
+  a.xcv = cv;
+  const size_t xbytes = (size_t)R * cv * 16;
+  hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, P>), dim3(grid), dim3(256), xbytes, s, a);
 }
 
 // Inputs are normalised inside the projection for windows of up to

@@ -5,12 +5,14 @@
 // the matrix units).
 //
 // Both operands are K-contiguous: activations [M][K] and published weights
-// [N][K].  A BM x BN block tile is staged through LDS in BK = 64 slices,
-// double-buffered; each wave owns a WM x WN sub-tile made of 32x32 output
-// tiles of v_mfma_f32_32x32x16_bf16.  Lane l of an MFMA reads row l%32 and 8
-// consecutive k at 8*(l/32) of each operand (one 16-byte LDS read), and holds
-// output rows 8*(j/4) + 4*(l/32) + j%4 of column l%32 in its accumulators.
-// Every output's K loop runs in the same order whatever M is.
+// [N][K].  Every output is a chain of v_mfma_f32_32x32x16_bf16 over 16-deep k
+// steps in increasing k: lane l of an MFMA reads row l%32 and 8 consecutive k
+// at 8*(l/32) of each operand, and holds output rows 8*(j/4) + 4*(l/32) + j%4
+// of column l%32 in its accumulators.  Two kernels share that order, so every
+// output's bits are the same whichever runs and whatever M is:
+// gemm_alt_kernel (256 x 256 tiles, an alternating two-group schedule with
+// LDS-direct operand copies) and gemm_kernel (smaller tiles, register-staged
+// copies, one pinned interleaved schedule).
 //
 // Epilogues: STORE (bf16 and optionally the fp32 sum), RESIDUAL
 // (h = bf16(h + bf16(acc))) and SWIGLU: the tile's columns alternate 32 gate
@@ -38,6 +40,44 @@ struct GemmArgs {
 
 __device__ __forceinline__ float silu_r(float g) { return rbf(g / (1.0f + expf(-g))); }
 
+// Epilogue of a wave's TM x TN 32x32 tiles at rows r0.., tile columns c0..:
+// lane l holds column l%32 and rows 8*(j/4) + 4*(l/32) + j%4 of each.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16_t (&acc)[TM][TN], int r0,
+                                           int c0, int lane) {
+  const int lr = lane & 31, hrow = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = r0 + i * 32 + 8 * (r >> 2) + hrow + (r & 3);
+      if (m >= a.M) continue;
+      if (EPI == GEMV_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < TN; j += 2) {
+          const int col = c0 + j * 32;  // gate tile column; up follows at +32
+          const int n = (col >> 6) * 32 + lr;
+          float g = rbf(acc[i][j][r]), u = rbf(acc[i][j + 1][r]);
+          a.out[(size_t)m * a.ldo + n] = f2bf(silu_r(g) * u);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = c0 + j * 32 + lr;
+          const float v = acc[i][j][r];
+          bf16_t* o = a.out + (size_t)m * a.ldo + n;
+          if (EPI == GEMV_STORE) {
+            *o = f2bf(v);
+            if (a.out32) a.out32[(size_t)m * a.ld32 + n] = v;
+          } else {
+            *o = f2bf(bf2f(*o) + rbf(v));
+          }
+        }
+      }
+    }
+  }
+}
+
 // Workgroup b runs on XCD b % 8; tiles are handed out so that each XCD
 // takes a contiguous run of tile indices, and within a run the row tiles of
 // one column tile are adjacent: the weight slice of a column tile is then
@@ -47,8 +87,10 @@ __device__ __forceinline__ int xcd_tile(int b, int nt) {
   return b < full ? (b % 8) * (nt / 8) + b / 8 : b;
 }
 
-// Register budget: two waves per SIMD (two workgroups per CU when a
-// workgroup has four waves).
+// A BM x BN block tile staged through LDS in BK-deep slices, double-buffered
+// (rows padded to BK + 8 elements); each wave owns a WM x WN sub-tile of
+// 32x32 MFMA tiles.  Register budget: two waves per SIMD (two workgroups per
+// CU when a workgroup has four waves).
 template <int BM, int BN, int WM, int WN, int EPI, int BK>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, (BM / WM) * (BN / WN) <= 4 ? 2 : 1)
 void gemm_kernel(GemmArgs a, int mtiles) {
@@ -203,38 +245,199 @@ void gemm_kernel(GemmArgs a, int mtiles) {
   }
   if (kt < nk) step(kt, 0);
 
-  // epilogue
-  const int hrow = (lane >> 5) * 4;
+  store_tile<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, lane);
+}
+
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles on an alternating schedule.  Eight waves, two per SIMD, in
+// two groups: group g (waves 4g .. 4g + 3, one per SIMD) owns output rows
+// 128g .. 128g + 127, each wave a 128 x 64 sub-tile.  Phases alternate: in one
+// a group's waves issue nothing but products of a whole 64-deep k-tile from
+// registers, while the other group's waves read their next k-tile's fragments
+// from LDS and issue the copies of a later k-tile; then the groups swap.  The
+// SIMD's matrix pipe is fed by one wave while its partner waits on memory, so
+// the LDS reads and copies stay off the products' path.
+//
+// Operand tiles go from global memory straight to LDS (16-byte LDS-direct
+// loads, one KiB = 8 rows of 128 bytes per copy), double-buffered: rows of
+// 64 k, chunk c of row r stored at chunk c ^ ((r >> 1) & 7), so a fragment
+// read (rows l%32, one chunk) touches every bank once per 16 lanes.  The
+// copies of tile kt + 2 go into tile kt's buffer as soon as both groups have
+// read it: activation rows 0-127 (read by group 0 only) by group 1 while it
+// reads tile kt, the rest by group 0 in the next phase.  The products run in
+// the same order as gemm_kernel's, so the two give the same bits.
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Phase boundary: nothing is scheduled across it, this wave's LDS reads
+// have completed, then all waves meet.  (__syncthreads would also wait for
+// the copies in flight.)
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_copies() {  // at most N of this wave's copies in flight
+  __builtin_amdgcn_sched_barrier(0);
+  if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles) {
+  constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, TM = 4, TN = 2, KS = 4;
+  constexpr int TILE = BM * BK * 2;  // bytes of one operand k-tile; LDS: A0 A1 B0 B1
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  uint8_t* lds = (uint8_t*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int grp = wave >> 2, q = wave & 3;
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (t % mtiles) * BM, n0 = (t / mtiles) * BN;
+
+  // Copy c of an operand tile covers rows 8c .. 8c + 7; lane l writes slot l:
+  // row 8c + l/8, stored chunk l%8, holding logical chunk
+  // (l%8) ^ ((row >> 1) & 7) = (l%8) ^ ((4(c%2) + l/16) & 7).
+  const int lrow = lane >> 3;
+  const uint32_t xs0 = (uint32_t)(((lane & 7) ^ ((lane >> 4) & 7)) * 16);
+  const uint32_t xs1 = (uint32_t)(((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 16);
+  const uint8_t* gA = (const uint8_t*)(a.A + (size_t)m0 * a.lda);
+  const uint32_t rsA = (uint32_t)a.lda * 2, rsB = (uint32_t)a.K * 2;
+  const uint8_t* gB[2];
+  if (EPI == GEMV_SWIGLU) {  // tile columns alternate 32 gate and 32 up rows
+    gB[0] = (const uint8_t*)(a.gate + (size_t)(n0 / 2) * a.K);
+    gB[1] = (const uint8_t*)(a.up + (size_t)(n0 / 2) * a.K);
+  } else {  // the tile lies inside one segment (boundaries are multiples of 256)
+    const bf16_t* W = a.seg[0].W;
+    int sb = a.seg[0].n_begin;
+    for (int sg = 1; sg < a.nseg; ++sg)
+      if (n0 >= a.seg[sg].n_begin) { W = a.seg[sg].W; sb = a.seg[sg].n_begin; }
+    gB[0] = gB[1] = (const uint8_t*)(W + (size_t)(n0 - sb) * a.K);
+  }
+  const int mlast = a.M - 1 - m0;  // activation rows past M re-read the last row
+  auto copy = [&](int kt, bool opA, int c) {
+    const int row = 8 * c + lrow;
+    const uint8_t* b;
+    uint32_t go;
+    if (opA) {
+      b = gA;
+      go = (uint32_t)min(row, mlast) * rsA;
+    } else if (EPI == GEMV_SWIGLU) {
+      b = gB[(c >> 2) & 1];
+      go = (uint32_t)((c >> 3) * 32 + (row & 31)) * rsB;
+    } else {
+      b = gB[0];
+      go = (uint32_t)row * rsB;
+    }
+    go += ((c & 1) ? xs1 : xs0) + (uint32_t)kt * (BK * 2);
+    const int loff = (opA ? 0 : 2 * TILE) + (kt & 1) * TILE + c * 1024;
+    __builtin_amdgcn_global_load_lds((const void*)(b + go), (lds_ptr_t)(lds + loff), 16, 0, 0);
+  };
+
+  f32x16_t acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * WM + i * 32 + 8 * (r >> 2) + hrow + (r & 3);
-      if (m >= a.M) continue;
-      if (EPI == GEMV_SWIGLU) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int j = 0; j < TN; j += 2) {
-          const int col = n0 + wn * WN + j * 32;  // gate tile column; up follows at +32
-          const int n = (col >> 6) * 32 + lr;
-          float g = rbf(acc[i][j][r]), u = rbf(acc[i][j + 1][r]);
-          a.out[(size_t)m * a.ldo + n] = f2bf(silu_r(g) * u);
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragment of a 32-row tile: lane l reads row l%32, logical chunk
+  // 2ks + l/32, stored at that ^ ((l%32 >> 1) & 7)
+  const int lr = lane & 31, swz = (lr >> 1) & 7;
+  uint32_t fa_off[KS], fb_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t ch = (uint32_t)(((2 * ks + (lane >> 5)) ^ swz) * 16);
+    fa_off[ks] = (uint32_t)(grp * WM + lr) * 128 + ch;
+    fb_off[ks] = 2 * TILE + (uint32_t)(q * WN + lr) * 128 + ch;
+  }
+  bf16x8_t fa[KS][TM], fb[KS][TN];
+  auto load_frags = [&](int kt) {
+    const uint32_t bo = (uint32_t)(kt & 1) * TILE;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[ks][i] = *(const bf16x8_t*)(lds + fa_off[ks] + bo + i * 32 * 128);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[ks][j] = *(const bf16x8_t*)(lds + fb_off[ks] + bo + j * 32 * 128);
+    }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = a.K / BK;
+  // k-tiles 0 and 1: waves 0-3 copy the activation tiles, 4-7 the weights
+  for (int k = 0; k < 2 && k < nk; ++k)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) copy(k, grp == 0, q * 8 + i);
+  wait_copies<0>();
+  phase_barrier();
+  // Phase 2kt: group 0 multiplies tile kt, group 1 reads its fragments (and
+  // copies tile kt + 2's activation rows 0-127).  Phase 2kt + 1: group 1
+  // multiplies tile kt, group 0 copies the rest of tile kt + 2 and reads tile
+  // kt + 1's fragments.  Each wave waits for its own copies of a tile before
+  // the barrier that precedes the tile's first reader.
+  if (grp == 0) {
+    load_frags(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      multiply();
+      wait_copies<0>();
+      phase_barrier();
+      if (kt + 2 < nk) {
+        if (kt == 0) {  // in phase 0 group 0 was still reading tile 0's rows 0-127
+#pragma unroll
+          for (int i = 0; i < 4; ++i) copy(kt + 2, true, q * 4 + i);
         }
-      } else {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int n = n0 + wn * WN + j * 32 + lr;
-          const float v = acc[i][j][r];
-          bf16_t* o = a.out + (size_t)m * a.ldo + n;
-          if (EPI == GEMV_STORE) {
-            *o = f2bf(v);
-            if (a.out32) a.out32[(size_t)m * a.ld32 + n] = v;
-          } else {
-            *o = f2bf(bf2f(*o) + rbf(v));
-          }
-        }
+        for (int i = 0; i < 4; ++i) copy(kt + 2, true, 16 + q * 4 + i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) copy(kt + 2, false, q * 8 + i);
       }
+      if (kt + 1 < nk) load_frags(kt + 1);
+      phase_barrier();
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt >= 1 && kt + 2 < nk;
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) copy(kt + 2, true, q * 4 + i);
+      }
+      load_frags(kt);
+      if (more) wait_copies<4>();  // tile kt + 1's copies done, kt + 2's may fly
+      else wait_copies<0>();
+      phase_barrier();
+      multiply();
+      phase_barrier();
     }
   }
+
+  store_tile<EPI, TM, TN>(a, acc, m0 + grp * WM, n0 + q * WN, lane);
+}
+
+template <int EPI>
+void launch_alt(const GemmArgs& a, int ncols, hipStream_t s) {
+  const int mtiles = (a.M + 255) / 256;
+  const int nt = (ncols / 256) * mtiles;
+  const size_t lds = (size_t)4 * 256 * 64 * 2;
+  static bool attr = false;  // one-time opt-in above the default dynamic LDS limit
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)gemm_alt_kernel<EPI>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL((gemm_alt_kernel<EPI>), dim3(nt), dim3(512), lds, s, a, mtiles);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int BK = 64>
@@ -268,12 +471,13 @@ static int cu_count() {
 }
 
 // ncols: tile columns (N, or 2F for SWIGLU); a multiple of 128.  Widths that
-// are multiples of 256 take 256 x 256 tiles (eight waves of 128 x 64), which
-// halve the LDS and L2 traffic per product of the 128 x 128 tiles; when the
+// are multiples of 256 take 256 x 256 tiles on the alternating schedule when
+// every weight segment starts at a multiple of 256 (SwiGLU always); when the
 // 256-wide tiles would leave the last round of workgroups mostly empty, 256 x
-// 128 tiles (eight waves of 64 x 64, about 15% slower per product) fill the
-// CUs better.  The split of K into 64-deep tiles and 16-deep MFMA steps, and so
-// every output's bits, is the same for all of them.
+// 128 tiles (eight waves of 64 x 64, about 28% slower per product) fill the
+// CUs better; other widths take 128 x 128 tiles.  The split of K into 64-deep
+// tiles and 16-deep MFMA steps, and so every output's bits, is the same for
+// all of them.
 void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* seg, int nseg,
                  const void* gate, const void* up, void* out, int ldo, float* out32, int ld32,
                  int ncols, hipStream_t s) {
@@ -290,25 +494,28 @@ void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* s
   a.ldo = ldo;
   a.out32 = out32;
   a.ld32 = ld32;
-  const bool big = ncols % 256 == 0;
+  bool big = ncols % 256 == 0;
+  if (epi != GEMV_SWIGLU)
+    for (int i = 0; i < nseg; ++i) big = big && seg[i].n_begin % 256 == 0;
   bool narrow = false;
   if (big) {
     const int cus = cu_count(), mt = (M + 255) / 256;
     const int rounds256 = ((ncols / 256) * mt + cus - 1) / cus;
     const int rounds128 = ((ncols / 128) * mt + cus - 1) / cus;
-    narrow = rounds128 * 0.575 < rounds256 * 1.0;
+    narrow = rounds128 * 0.72 < rounds256 * 1.0;
   }
+  const bool wide = ncols % 256 == 0;
   if (epi == GEMV_STORE) {
-    if (narrow) launch_tile<256, 128, 64, 64, GEMV_STORE>(a, ncols, s);
-    else if (big) launch_tile<256, 256, 128, 64, GEMV_STORE>(a, ncols, s);
+    if (big && !narrow) launch_alt<GEMV_STORE>(a, ncols, s);
+    else if (wide) launch_tile<256, 128, 64, 64, GEMV_STORE>(a, ncols, s);
     else launch_tile<128, 128, 64, 64, GEMV_STORE>(a, ncols, s);
   } else if (epi == GEMV_RESIDUAL) {
-    if (narrow) launch_tile<256, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
-    else if (big) launch_tile<256, 256, 128, 64, GEMV_RESIDUAL>(a, ncols, s);
+    if (big && !narrow) launch_alt<GEMV_RESIDUAL>(a, ncols, s);
+    else if (wide) launch_tile<256, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
     else launch_tile<128, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
   } else {
-    if (narrow) launch_tile<256, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
-    else if (big) launch_tile<256, 256, 128, 64, GEMV_SWIGLU>(a, ncols, s);
+    if (big && !narrow) launch_alt<GEMV_SWIGLU>(a, ncols, s);
+    else if (wide) launch_tile<256, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
     else launch_tile<128, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
   }
 }

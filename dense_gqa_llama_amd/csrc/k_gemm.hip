@@ -472,12 +472,24 @@ static int cu_count() {
 
 // ncols: tile columns (N, or 2F for SWIGLU); a multiple of 128.  Widths that
 // are multiples of 256 take 256 x 256 tiles on the alternating schedule when
-// every weight segment starts at a multiple of 256 (SwiGLU always); when the
-// 256-wide tiles would leave the last round of workgroups mostly empty, 256 x
-// 128 tiles (eight waves of 64 x 64, about 28% slower per product) fill the
-// CUs better; other widths take 128 x 128 tiles.  The split of K into 64-deep
-// tiles and 16-deep MFMA steps, and so every output's bits, is the same for
-// all of them.
+// every weight segment starts at a multiple of 256 (SwiGLU always), unless
+// 256 x 128 tiles (eight waves of 64 x 64, about 0.72 the time of a 256 x 256
+// tile) would fill the CUs in fewer rounds' worth of time.  Other widths take
+// 128 x 128 tiles.  The split of K into 64-deep tiles and 16-deep MFMA steps,
+// and so every output's bits, is the same for all of them.
+template <int EPI>
+static void launch_epi(GemmArgs a, int ncols, bool aligned, hipStream_t s) {
+  if (ncols % 256 != 0) {
+    launch_tile<128, 128, 64, 64, EPI>(a, ncols, s);
+    return;
+  }
+  const int cus = cu_count(), mt = (a.M + 255) / 256, ct = ncols / 256;
+  const int rounds256 = (ct * mt + cus - 1) / cus;
+  const int rounds128 = (2 * ct * mt + cus - 1) / cus;
+  if (!aligned || rounds128 * 0.72 < rounds256) launch_tile<256, 128, 64, 64, EPI>(a, ncols, s);
+  else launch_alt<EPI>(a, ncols, s);
+}
+
 void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* seg, int nseg,
                  const void* gate, const void* up, void* out, int ldo, float* out32, int ld32,
                  int ncols, hipStream_t s) {
@@ -494,28 +506,10 @@ void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* s
   a.ldo = ldo;
   a.out32 = out32;
   a.ld32 = ld32;
-  bool big = ncols % 256 == 0;
+  bool aligned = true;  // every 256-wide tile lies in one weight segment
   if (epi != GEMV_SWIGLU)
-    for (int i = 0; i < nseg; ++i) big = big && seg[i].n_begin % 256 == 0;
-  bool narrow = false;
-  if (big) {
-    const int cus = cu_count(), mt = (M + 255) / 256;
-    const int rounds256 = ((ncols / 256) * mt + cus - 1) / cus;
-    const int rounds128 = ((ncols / 128) * mt + cus - 1) / cus;
-    narrow = rounds128 * 0.72 < rounds256 * 1.0;
-  }
-  const bool wide = ncols % 256 == 0;
-  if (epi == GEMV_STORE) {
-    if (big && !narrow) launch_alt<GEMV_STORE>(a, ncols, s);
-    else if (wide) launch_tile<256, 128, 64, 64, GEMV_STORE>(a, ncols, s);
-    else launch_tile<128, 128, 64, 64, GEMV_STORE>(a, ncols, s);
-  } else if (epi == GEMV_RESIDUAL) {
-    if (big && !narrow) launch_alt<GEMV_RESIDUAL>(a, ncols, s);
-    else if (wide) launch_tile<256, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
-    else launch_tile<128, 128, 64, 64, GEMV_RESIDUAL>(a, ncols, s);
-  } else {
-    if (big && !narrow) launch_alt<GEMV_SWIGLU>(a, ncols, s);
-    else if (wide) launch_tile<256, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
-    else launch_tile<128, 128, 64, 64, GEMV_SWIGLU>(a, ncols, s);
-  }
+    for (int i = 0; i < nseg; ++i) aligned = aligned && seg[i].n_begin % 256 == 0;
+  if (epi == GEMV_STORE) launch_epi<GEMV_STORE>(a, ncols, aligned, s);
+  else if (epi == GEMV_RESIDUAL) launch_epi<GEMV_RESIDUAL>(a, ncols, aligned, s);
+  else launch_epi<GEMV_SWIGLU>(a, ncols, aligned, s);
 }

@@ -25,6 +25,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 STREAMS = (2, 12)      # concurrent sequences sharing every decode round
+WINDOWS = (1, 7, 16)    # decode window widths timed
+WINDOW_STEPS = 8
+DRAFT_K = 7             # proposals per drafted round
+DRAFT_ROUNDS = 8
 STREAM_ROUNDS = 32
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes of the dominant kernel from rocprofv3 counters, with the digest of
@@ -275,6 +279,59 @@ def main():
         del seqs
     torch.cuda.empty_cache()
 
+    # decode windows (teacher-forced rows after the prompt): one window of
+    # `rows` rows per step, the verification step of drafted decoding
+    windows = []
+    wseq = model.new_sequence(cap)  # P + 16 * WINDOW_STEPS positions fit
+    for rows in WINDOWS:
+        wseq.set_length(0)
+        model.prefill(wseq, tokens=prompt, want_logits=False)
+        toks = sd.tokens(rows * WINDOW_STEPS, 4700 + rows, 0, g.vocab)
+        model.decode([wseq], tokens=toks[:rows], rows=rows, want_logits=False)  # warm
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(1, WINDOW_STEPS):
+            model.decode([wseq], tokens=toks[i * rows:(i + 1) * rows], rows=rows,
+                         want_logits=False)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / (WINDOW_STEPS - 1)
+        windows.append({"rows": rows, "ms_per_window": round(ms, 3)})
+        log(f"{rows}-row windows: {ms:.2f} ms each")
+    del wseq
+
+    # drafted greedy rounds with the looped 3B-shaped model (same vocabulary)
+    # drafting; with random weights its proposals are rarely taken, so this
+    # measures the rounds' cost, not a drafted speed-up
+    gd = config(4)
+    wd = sd.weights(gd)
+    torch.cuda.synchronize()
+    dmodel = L.Model(gd, wd, max_positions=cap, max_chunk_rows=P, max_window_rows=1, max_seqs=1)
+    tseq, dseq = model.new_sequence(cap), dmodel.new_sequence(cap)
+    last = model.prefill(tseq, tokens=prompt, want_logits=False)["next"]
+    dmodel.prefill(dseq, tokens=prompt, want_logits=False)
+    model.draft_round(tseq, dmodel, dseq, DRAFT_K, last)  # warm
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ntok = taken = 0
+    for _ in range(DRAFT_ROUNDS):
+        toks, m = model.draft_round(tseq, dmodel, dseq, DRAFT_K, last)
+        ntok += m
+        taken += m - 1
+        last = toks[m - 1:m].clone()
+    torch.cuda.synchronize()
+    draft_s = time.perf_counter() - t0
+    drafting = {"draft": "looped model, 22 blocks x 2 loops, hidden 3072, vocab 166912 "
+                         "(random weights)",
+                "n_draft": DRAFT_K, "rounds": DRAFT_ROUNDS, "tokens": ntok,
+                "proposals_taken": round(taken / (DRAFT_K * DRAFT_ROUNDS), 4),
+                "ms_per_round": round(draft_s * 1e3 / DRAFT_ROUNDS, 3),
+                "tok_s": round(ntok / draft_s, 2)}
+    log(f"drafted rounds: {drafting}")
+    del dmodel, wd, tseq, dseq
+    torch.cuda.empty_cache()
+
     # seeded sampling of one logit row (temperature 0.6, top_k 20, top_p 0.95)
     sq = model.new_sequence(cap)
     lg = model.prefill(sq, tokens=prompt)["logits"]
@@ -323,6 +380,8 @@ def main():
                               "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                               "ms_per_chunk": round(attn_ms, 3)},
         "streams": streams,
+        "windows": windows,
+        "drafting": drafting,
         "sampling": {"us_per_row": round(sample_us, 2), "temperature": 0.6, "top_k": 20,
                      "top_p": 0.95},
         "roofline": {"bound": "hbm", "kernel": "decode gate/up projection + SwiGLU (R=1)",

@@ -71,6 +71,8 @@ _SIGS = {
     "llama_check_finite": (ctypes.c_int, [_P, _P]),
     "llama_sample": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                     ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
+    "llama_draft_round": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                          ctypes.POINTER(ctypes.c_int32), _P]),
     "llama_set_timing": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32]),
     "llama_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(ctypes.c_int64)]),
@@ -191,6 +193,15 @@ def llama_check_finite(model, stream=None):
 def llama_sample(model, logits_bf16, rows, ld, temperature, top_k, top_p, u, tokens, stream=None):
     return _check(lib.llama_sample(model, logits_bf16, rows, ld, temperature, top_k, top_p, u,
                                    tokens, stream))
+
+
+def llama_draft_round(target, target_kv, draft, draft_kv, n_draft, last_token, tokens_out,
+                      stream=None):
+    """Returns the number of tokens the round wrote to tokens_out."""
+    n = ctypes.c_int32(0)
+    _check(lib.llama_draft_round(target, target_kv, draft, draft_kv, n_draft, last_token,
+                                 tokens_out, ctypes.byref(n), stream))
+    return n.value
 
 
 TIMING = {"off": 0, "gate_up": 1, "down": 2, "qkv": 3, "o": 4, "lm_head": 5, "attn": 6,

@@ -1,5 +1,5 @@
 // Glue kernels of the forward step: embedding gather, RMSNorm, RoPE with the
-// cache write, greedy argmax.  Rounding points follow the pull request
+// cache write, greedy argmax, the acceptance of a drafted round.  Rounding points follow the pull request
 // "llama: Nanbeige4.3-33B on Metal, the bf16 release served as published",
 // section "How".
 #include "common.h"
@@ -208,4 +208,30 @@ void launch_argmax(const void* logits, int V, int ld, int rows, float* pv, int* 
   hipLaunchKernelGGL(argmax_partial_kernel, dim3(nchunk, rows), dim3(256), 0, s,
                      (const bf16_t*)logits, V, ld, pv, pi, nchunk);
   hipLaunchKernelGGL(argmax_final_kernel, dim3(rows), dim3(64), 0, s, pv, pi, nchunk, out, flag);
+}
+
+// ------------------------------------------------------- drafted rounds ----
+// One drafted round (issue "A llama family on Metal", follow-ups: a smaller
+// Llama on the same tokenizer drafting with replies unchanged; pull request,
+// reply "Drafting": drafted greedy equals plain greedy).  win = [last, d_1 ..
+// d_k] are the window's input tokens (d_i the draft's proposals), t[0..k] the
+// target's greedy tokens after each of them.  The target agrees with the
+// first a proposals where d_{i+1} == t_i for all i < a (a valid id); the
+// round yields d_1 .. d_a and then t_a, the target's own next token, so the
+// reply is the one plain greedy steps give.  One lane; writes a to *count.
+__global__ void draft_accept_kernel(const int32_t* __restrict__ win, const int32_t* __restrict__ t,
+                                    int k, int32_t* __restrict__ out, int32_t* __restrict__ count) {
+  if (threadIdx.x != 0) return;
+  int a = 0;
+  while (a < k && t[a] >= 0 && win[a + 1] == t[a]) {
+    out[a] = t[a];
+    ++a;
+  }
+  out[a] = t[a];
+  *count = a;
+}
+
+void launch_draft_accept(const int32_t* win, const int32_t* t, int k, int32_t* out,
+                         int32_t* count, hipStream_t s) {
+  hipLaunchKernelGGL(draft_accept_kernel, dim3(1), dim3(64), 0, s, win, t, k, out, count);
 }

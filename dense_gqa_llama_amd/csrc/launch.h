@@ -37,6 +37,10 @@ void launch_sample(const void* logits, int V, int64_t ld, int rows, int k, float
                    int* flag, hipStream_t s);
 void launch_argmax(const void* logits, int V, int ld, int rows, float* pv, int* pi, int32_t* out,
                    int* flag, hipStream_t s);
+// Acceptance of a drafted round: win[0..k] window inputs, t[0..k] the
+// target's greedy tokens; out[0..a] the round's tokens, *count = a.
+void launch_draft_accept(const int32_t* win, const int32_t* t, int k, int32_t* out,
+                         int32_t* count, hipStream_t s);
 
 // Decode projections (1..16 rows).  Output columns [0, N) are the
 // concatenation of up to three weight matrices (segments), each [rows][K].

@@ -32,7 +32,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Device workspace carved into fixed regions.
 struct Layout {
-  size_t h, x, qkv, q, att, m, rope, logits, amx_v, amx_i, part, smp_v, smp_i, smp_bad, flag, total;
+  size_t h, x, qkv, q, att, m, rope, logits, amx_v, amx_i, part, smp_v, smp_i, smp_bad, draft, flag,
+      total;
 };
 
 struct Dims {
@@ -84,6 +85,7 @@ Layout layout_of(const Dims& d) {
   L.smp_v = take((size_t)LLAMA_SAMPLE_MAX_ROWS * nsc * LLAMA_SAMPLE_MAX_TOP_K * 4);
   L.smp_i = take((size_t)LLAMA_SAMPLE_MAX_ROWS * nsc * LLAMA_SAMPLE_MAX_TOP_K * 4);
   L.smp_bad = take((size_t)LLAMA_SAMPLE_MAX_ROWS * nsc * 4);
+  L.draft = take(3 * 32 * 4);  // a drafted round's window inputs, target tokens, count
   L.flag = take(256);
   L.total = off;
   return L;
@@ -560,6 +562,72 @@ int llama_decode_step(llama_model* m, llama_kv* const* kvs, int32_t n_seq,
   rc = dev_check("decode launch");
   if (rc) return rc;
   for (int i = 0; i < n_seq; ++i) kvs[i]->length += rows;
+  return LLAMA_OK;
+}
+
+int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* draft,
+                      llama_kv* draft_kv, int32_t n_draft, const int32_t* last_token_dev,
+                      int32_t* tokens_out_dev, int32_t* n_out, void* hip_stream) {
+  if (!target || !draft) return fail(LLAMA_E_ARG, "model is NULL");
+  if (target == draft) return fail(LLAMA_E_ARG, "the draft model is the target model");
+  int rc = check_kv(target, target_kv);
+  if (rc) return rc;
+  rc = check_kv(draft, draft_kv);
+  if (rc) return rc;
+  if (!last_token_dev || !tokens_out_dev || !n_out) return fail(LLAMA_E_ARG, "NULL argument");
+  if (!target->d.V || target->d.V != draft->d.V)
+    return fail(LLAMA_E_ARG, "vocabularies differ (%d and %d)", target->d.V, draft->d.V);
+  if (n_draft < 1 || n_draft + 1 > target->cfg.max_window_rows)
+    return fail(LLAMA_E_ARG, "n_draft %d outside 1..%d (the target's window less one)", n_draft,
+                target->cfg.max_window_rows - 1);
+  const int p = target_kv->length;
+  if (draft_kv->length != p)
+    return fail(LLAMA_E_POSITION, "the draft cache holds %d positions, the target's %d",
+                draft_kv->length, p);
+  if ((int64_t)p + n_draft + 1 > target_kv->max_positions)
+    return fail(LLAMA_E_CAPACITY, "positions %d..%d pass the target cache's %d", p, p + n_draft,
+                target_kv->max_positions);
+  if ((int64_t)p + n_draft + 1 > draft_kv->max_positions)
+    return fail(LLAMA_E_CAPACITY, "positions %d..%d pass the draft cache's %d", p, p + n_draft,
+                draft_kv->max_positions);
+  rc = check_capture(target, n_draft + 1);
+  if (rc) return rc;
+  rc = check_capture(draft, 1);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)hip_stream;
+  int32_t* win = target->at<int32_t>(target->L.draft);  // [0..k]: last, d_1 .. d_k
+  int32_t* tt = win + 32;                                 // target's greedy tokens
+  int32_t* cnt = win + 64;
+  if (hipMemcpyAsync(win, last_token_dev, 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return dev_check("drafted round copy");
+  // the draft's greedy proposals, one row at a time, each fed back
+  for (int i = 0; i < n_draft; ++i) {
+    rc = llama_decode_step(draft, &draft_kv, 1, win + i, nullptr, 1, nullptr, nullptr, nullptr,
+                           win + i + 1, s);
+    if (rc) return rc;
+  }
+  // the target's verdict on all of them in one window
+  rc = llama_decode_step(target, &target_kv, 1, win, nullptr, n_draft + 1, nullptr, nullptr,
+                         nullptr, tt, s);
+  if (rc) return rc;
+  launch_draft_accept(win, tt, n_draft, tokens_out_dev, cnt, s);
+  rc = dev_check("drafted round acceptance");
+  if (rc) return rc;
+  int32_t a = 0;
+  if (hipMemcpyAsync(&a, cnt, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return dev_check("drafted round count");
+  // both caches keep the inputs last, d_1 .. d_a; with every proposal taken
+  // the draft has not yet read d_k, so it reads it now (its token unused)
+  target_kv->length = p + a + 1;
+  if (a == n_draft) {
+    rc = llama_decode_step(draft, &draft_kv, 1, win + n_draft, nullptr, 1, nullptr, nullptr,
+                           nullptr, tt, s);
+    if (rc) return rc;
+  } else {
+    draft_kv->length = p + a + 1;
+  }
+  *n_out = a + 1;
   return LLAMA_OK;
 }
 

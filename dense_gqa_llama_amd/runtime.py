@@ -110,6 +110,18 @@ class Model:
                        int(top_k), float(top_p), u.data_ptr(), out.data_ptr(), _stream())
         return out
 
+    def draft_round(self, seq, draft, draft_seq, n_draft, last_token, out=None):
+        """One drafted greedy round (``llama_draft_round``): ``draft`` (a Model
+        on the same vocabulary) proposes ``n_draft`` tokens after
+        ``last_token`` (int32 [1] on the device) and this model verifies them
+        in one window.  Returns (tokens, n): the round's n tokens are
+        tokens[:n]; tokens[n - 1] is the next round's input."""
+        if out is None:
+            out = torch.empty(n_draft + 1, dtype=torch.int32, device=last_token.device)
+        n = B.llama_draft_round(self.handle, seq.handle, draft.handle, draft_seq.handle,
+                                int(n_draft), last_token.data_ptr(), out.data_ptr(), _stream())
+        return out, n
+
     def check_finite(self):
         B.llama_check_finite(self.handle, _stream())
 

@@ -204,6 +204,32 @@ int llama_sample(llama_model* model, const void* logits_bf16_dev, int32_t rows, 
                  float temperature, int32_t top_k, float top_p, const float* u_dev,
                  int32_t* tokens_dev, void* hip_stream);
 
+/* One round of drafted greedy decoding (issue "A llama family on Metal:
+ * Nanbeige4.3-33B served from its bf16 release", follow-ups: a smaller Llama
+ * on the same tokenizer drafting for the served model with replies
+ * unchanged; pull request "llama: Nanbeige4.3-33B on Metal, the bf16 release
+ * served as published", reply "Drafting": drafted greedy equals plain
+ * greedy).  Both caches hold the same p positions (the tokens before
+ * last_token_dev[0], the next input, int32 on the device).  The draft model
+ * proposes d_1 .. d_n by n_draft greedy one-row steps from that token; the
+ * target reads [last, d_1 .. d_n] as one window at positions p .. p + n and
+ * draws its greedy token after each; the round yields the a leading
+ * proposals the target agrees with, then the target's own token after them:
+ * tokens_out_dev[0 .. a] (int32, device, room for n_draft + 1), *n_out = a + 1
+ * (host).  Windows equal one-row steps bit for bit, so the reply equals the
+ * target's plain greedy steps whatever the draft proposes.  Afterwards both
+ * caches hold p + a + 1 positions (last, d_1 .. d_a) and the next round's
+ * input is tokens_out_dev[a].  n_draft 1..(target max_window_rows - 1); both
+ * models have the same vocabulary; both caches need room for p + n_draft + 1
+ * positions.  Refusals (LLAMA_E_ARG, LLAMA_E_POSITION, LLAMA_E_CAPACITY)
+ * change nothing.  Unlike the other step calls it synchronises hip_stream
+ * once, to read a; both models' work runs on that stream and the target's
+ * workspace holds the round's token buffers.  A non-finite logit row shows
+ * as a -1 token and in llama_check_finite of the model that met it. */
+int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* draft,
+                      llama_kv* draft_kv, int32_t n_draft, const int32_t* last_token_dev,
+                      int32_t* tokens_out_dev, int32_t* n_out, void* hip_stream);
+
 /* Synchronises hip_stream, then reports LLAMA_E_NONFINITE if any greedy or
  * sampled draw since the last call met a non-finite logit row (and clears
  * the flag), else LLAMA_OK. */

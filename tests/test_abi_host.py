@@ -184,3 +184,41 @@ def test_sampling_refusals():
         expect(B.LLAMA_E_ARG, B.llama_sample, m2, FAKE, 1, 128, 1.0, 1, 1.0, FAKE, FAKE)
     finally:
         B.llama_free(m2)
+
+
+def test_draft_round_refusals():
+    """llama_draft_round checks both models and caches before it enqueues
+    anything: same vocabulary, a window that fits, caches of equal length
+    with room for the round, and refusals leave the lengths as they were."""
+    g = CONFIGS[1]
+    t, _ = load(g, max_chunk_rows=64, max_window_rows=8)
+    d, _ = load(g, max_chunk_rows=64, max_window_rows=1)
+    g4 = CONFIGS[4]
+    other, _ = load(g4, max_chunk_rows=16, max_window_rows=1)
+    try:
+        tkv = B.llama_kv_alloc(t, 64, FAKE, B.llama_kv_bytes(t, 64))
+        dkv = B.llama_kv_alloc(d, 32, FAKE, B.llama_kv_bytes(d, 32))
+        okv = B.llama_kv_alloc(other, 64, FAKE, B.llama_kv_bytes(other, 64))
+
+        def call(target=t, target_kv=tkv, draft=d, draft_kv=dkv, n=4, last=FAKE, out=FAKE):
+            return B.llama_draft_round(target, target_kv, draft, draft_kv, n, last, out)
+        for kw in (dict(n=0), dict(n=8), dict(last=None), dict(out=None), dict(target=None),
+                   dict(draft=t, draft_kv=tkv), dict(draft_kv=tkv), dict(target_kv=dkv),
+                   dict(draft=other, draft_kv=okv)):
+            expect(B.LLAMA_E_ARG, call, **kw)
+        B.llama_kv_set_length(dkv, 3)
+        expect(B.LLAMA_E_POSITION, call)
+        B.llama_kv_set_length(tkv, 27)
+        B.llama_kv_set_length(dkv, 27)
+        expect(B.LLAMA_E_CAPACITY, call, n=5)  # the draft cache ends at 32
+        dkv2 = B.llama_kv_alloc(d, 128, FAKE, B.llama_kv_bytes(d, 128))
+        B.llama_kv_set_length(tkv, 60)
+        B.llama_kv_set_length(dkv2, 60)
+        expect(B.LLAMA_E_CAPACITY, call, draft_kv=dkv2, n=4)  # the target cache ends at 64
+        assert B.llama_kv_length(tkv) == 60 and B.llama_kv_length(dkv2) == 60
+        assert B.llama_kv_length(dkv) == 27
+        for kv in (tkv, dkv, dkv2, okv):
+            B.llama_kv_free(kv)
+    finally:
+        for m in (t, d, other):
+            B.llama_free(m)

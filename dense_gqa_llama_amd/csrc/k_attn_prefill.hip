@@ -67,9 +67,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
   __shared__ int sBadW[2][4];           // some slot of the tile is flagged (per staging wave)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // heaviest row blocks first: block x covers rows of block (nblk - 1 - x)
-  const int rb = gridDim.x - 1 - blockIdx.x;
-  const int h = blockIdx.y, g = h / (nq / nkv);
+  // Heaviest row blocks first over the whole grid (longest-first keeps the
+  // last round short).  Workgroup b runs on XCD b % 8: with eight KV heads,
+  // XCD x takes the query heads of KV head x, so each XCD's L2 holds one
+  // head's keys and values.
+  const int nblk = (rows + QT - 1) / QT, G = nq / nkv;
+  int rb, h;
+  if (nkv == 8) {
+    const int j = blockIdx.x / 8;
+    rb = nblk - 1 - j / G;
+    h = (blockIdx.x % 8) * G + j % G;
+  } else {
+    rb = nblk - 1 - blockIdx.x / nq;
+    h = blockIdx.x % nq;
+  }
+  const int g = h / G;
   const int r0 = rb * QT;
   const int lq = lane & 31, half = lane >> 5;
   const int qrow = r0 + wave * 32 + lq;               // this lane's query row in the chunk
@@ -309,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
 // already holding positions [0, pos0 + rows); out: [rows][nq][d].
 void launch_attn_prefill(const void* q, const void* kc, const void* vc, int rows, int pos0, int nq,
                          int nkv, int d, void* out, hipStream_t s) {
-  dim3 grid((rows + QT - 1) / QT, nq);
+  dim3 grid((rows + QT - 1) / QT * nq);
   if (d == 64)
     hipLaunchKernelGGL(attn_prefill_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)q,
                        (const bf16_t*)kc, (const bf16_t*)vc, rows, pos0, nq, nkv, (bf16_t*)out);

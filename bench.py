@@ -29,6 +29,8 @@ WINDOWS = (1, 7, 16)    # decode window widths timed
 WINDOW_STEPS = 8
 DRAFT_K = 7             # proposals per drafted round
 DRAFT_ROUNDS = 8
+LONG_T = 131071         # cache positions before the long-context rounds
+LONG_ROUNDS = 8
 STREAM_ROUNDS = 32
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 # HBM bytes of the dominant kernel from rocprofv3 counters, with the digest of
@@ -186,7 +188,7 @@ def main():
     log(f"generating {g.params() * 2 / 2**30:.2f} GiB of weights on the GPU")
     w = sd.weights(g)
     torch.cuda.synchronize()
-    model = L.Model(g, w, max_positions=cap, max_chunk_rows=P, max_window_rows=16,
+    model = L.Model(g, w, max_positions=max(cap, LONG_T + LONG_ROUNDS + 1), max_chunk_rows=P, max_window_rows=16,
                     max_seqs=STREAMS[-1])
     seq = model.new_sequence(cap)
     prompt = sd.tokens(P, g.prompt_seeds[0], 0, g.vocab)
@@ -332,6 +334,42 @@ def main():
     del dmodel, wd, tseq, dseq
     torch.cuda.empty_cache()
 
+    # long-context decode rounds (the 131k workload's shape): two sequences
+    # whose caches hold LONG_T synthetic positions (keys and values ~N(0, 1))
+    # share every round; prefilling 131k real tokens would take minutes
+    gl = config(5)
+    lseqs = [model.new_sequence(LONG_T + LONG_ROUNDS + 1) for _ in range(2)]
+    from synth import normal_bf16_dev
+    for i, sq in enumerate(lseqs):
+        normal_bf16_dev(sq.buf.data_ptr(), sq.buf.numel() // 2, 3005 + i, 0,
+                        stream=stream.cuda_stream)
+        sq.set_length(LONG_T)
+    ltok = sd.tokens(2, gl.prompt_seeds[0], 1, g.vocab)
+    model.decode(lseqs, tokens=ltok, want_logits=False, next_out=ltok)  # warm
+    torch.cuda.synchronize()
+    B.llama_set_timing(model.handle, "attn", 2 * g.n_exec * LONG_ROUNDS)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(LONG_ROUNDS):
+        model.decode(lseqs, tokens=ltok, want_logits=False, next_out=ltok)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ams, an = B.llama_timing_read(model.handle)
+    B.llama_set_timing(model.handle, "off")
+    lms = a.elapsed_time(b) / LONG_ROUNDS
+    T_avg = LONG_T + 1 + (LONG_ROUNDS - 1) / 2.0
+    kvp = g.kv_bytes_per_position()
+    lbytes = decode_bytes(g, T_avg) + (T_avg + 2) * kvp  # weights once, both caches
+    long_ctx = {"positions": LONG_T + 1, "sequences": 2, "ms_per_round": round(lms, 3),
+                "tok_s": round(2 / (lms / 1e3), 2),
+                "hbm_gbs": round(lbytes / (lms / 1e3) / 1e9, 1),
+                "attention_us_per_block": round(ams * 1e3 / max(an, 1), 2),
+                "attention_gbs": round(2 * (T_avg + 2) * kvp / g.n_exec
+                                       / (ams / max(an, 1) / 1e3) / 1e9, 1)}
+    log(f"long context: {long_ctx}")
+    del lseqs
+    torch.cuda.empty_cache()
+
     # seeded sampling of one logit row (temperature 0.6, top_k 20, top_p 0.95)
     sq = model.new_sequence(cap)
     lg = model.prefill(sq, tokens=prompt)["logits"]
@@ -381,6 +419,7 @@ def main():
                               "ms_per_chunk": round(attn_ms, 3)},
         "streams": streams,
         "windows": windows,
+        "long_context": long_ctx,
         "drafting": drafting,
         "sampling": {"us_per_row": round(sample_us, 2), "temperature": 0.6, "top_k": 20,
                      "top_p": 0.95},

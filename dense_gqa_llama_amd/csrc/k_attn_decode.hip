@@ -8,17 +8,20 @@
 // partition, and so every sum, depends only on p: a row computed inside a
 // window or beside other sequences equals the row computed alone.
 //
-// One workgroup per (block, KV head, row).  It walks its block in sub-blocks
-// of 64 slots: four lanes per slot read the slot's key row (256 contiguous
-// bytes for d = 128) and score it against the G query heads sharing the KV
-// head (fp32, v_dot2c_f32_bf16), an online softmax keeps the running max and
-// sum per head, and lanes per value dimension accumulate exp(s - m) v.  The
-// block's (max, sum, unnormalised output) is written as a partial.  A second
-// kernel, one workgroup per (query head, row), merges a row's blocks in block
-// order, o = sum_b e^(m_b - M) o_b / sum_b e^(m_b - M) l_b, rounded once to
-// bf16.  (The kernel boundary makes the partials visible across the chip's
-// separate L2s; merging inside the first kernel would need a device-scope
-// release in every workgroup.)
+// One workgroup per (block, KV head, row); its four waves each walk a fixed
+// quarter of the block on their own, 16 slots at a time, with the next two
+// tiles' keys and values in flight.  Scores come from one MFMA chain per tile,
+// S^T = K Q^T (v_mfma_f32_16x16x32_bf16: the tile's 16 key rows against the G
+// query heads sharing the KV head, padded to 16), so lane l holds head l%16 for
+// slots 4(l/16)..+3; an online softmax keeps each head's running max and sum;
+// lanes per value dimension pair accumulate exp(s - m) v in fp32 with the
+// weights broadcast from the score lanes.  The quarters' (max, sum, output)
+// are combined in quarter order into the block's partial.  A second kernel,
+// one workgroup per (query head, row), merges a row's blocks in block order,
+// o = sum_b e^(m_b - M) o_b / sum_b e^(m_b - M) l_b, rounded once to bf16.
+// (The kernel boundary makes the partials visible across the chip's separate
+// L2s; merging inside the first kernel would need a device-scope release in
+// every workgroup.)
 #include "common.h"
 #include "launch.h"
 
@@ -37,13 +40,14 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restrict__ q,
                                                           RowTable tab, int nq, int nkv,
                                                           float* __restrict__ part) {
-  constexpr int DP = D / 2;        // value pairs per head
-  constexpr int NG = 256 / DP;     // slot groups in the value pass
-  constexpr int DQ = D / 4;        // key dims per lane in the score pass
-  __shared__ __attribute__((aligned(16))) uint32_t qs[G][DP];
-  __shared__ float S[G][SUB];
-  __shared__ float Ms[G], Ls[G], As[G];
-  __shared__ float O[NG][G][D];
+  constexpr int TS = 16;        // slots per tile
+  constexpr int KST = D / 32;   // MFMA steps over the head dimension
+  constexpr int DP = D / 2;     // value pairs per head
+  constexpr int NSG = 64 / DP;  // slot groups in the value pass (1 for d = 128, 2 for 64)
+  constexpr int VPL = TS / NSG; // value slots per lane per tile
+  static_assert(G <= 16 && NSG * DP == 64, "decode attention geometry");
+  __shared__ float sm[4][G], sl[4][G];
+  __shared__ float so[4][G][D];
 
   const int b = blockIdx.x, g = blockIdx.y, rt = blockIdx.z;
   const int seq = rt / tab.rows_per_seq;
@@ -52,135 +56,156 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
   const int nb = p / kb + 1;
   if (b >= nb) return;  // uniform per workgroup
   const int start = b * kb, end = min(start + kb, p + 1);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ql = kb / 4;  // a multiple of 16
+  const int ws = start + wave * ql, we = min(ws + ql, end);  // this wave's slots
+  const int ntile = we > ws ? (we - ws + TS - 1) / TS : 0;
   const int kvd = nkv * D;
-
-  const int dp = tid % DP, grp = tid / DP;
   const float scale = 1.0f / sqrtf((float)D);
-  const bf16_t* kbase = tab.k[seq] + (size_t)g * D;
-  const uint32_t* vbase = (const uint32_t*)(tab.v[seq] + (size_t)g * D) + dp;
-  const int kslot = tid >> 2, qq = tid & 3;  // score pass: lanes 4k..4k+3 share slot k
-  constexpr int KPL = SUB / NG;              // value pass: slots per lane
 
-  // The key and value loads of a sub-block are issued together, one
-  // sub-block ahead of their use, so a block costs one memory round trip
-  // rather than three (query, keys, then values).
-  u32x4_t kreg[DQ / 8];
-  uint32_t vv[KPL];
-  auto issue = [&](int s0) {
-    const int nk = min(SUB, end - s0);
-    if (kslot < nk) {
-      const u32x4_t* krow = (const u32x4_t*)(kbase + (size_t)(s0 + kslot) * kvd + qq * DQ);
+  // Q^T fragments (MFMA B operand): lane l holds head l%16, dims 8(l/16) + 32i
+  const int hl = lane & 15, dq = (lane >> 4) * 8;
+  bf16x8_t qf[KST];
 #pragma unroll
-      for (int j = 0; j < DQ / 8; ++j) kreg[j] = krow[j];
+  for (int i = 0; i < KST; ++i) {
+    if (hl < G) {
+      qf[i] = *(const bf16x8_t*)(q + ((size_t)rt * nq + (size_t)g * G + hl) * D + 32 * i + dq);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[i][e] = (__bf16)0.0f;
     }
+  }
+  // K fragments (A operand): lane l holds slot l%16 of the tile, dims
+  // 8(l/16) + 32i; values: lane l holds pair l%DP of slots l/DP + NSG*j.
+  // Slots past the wave's range re-read its last slot (never used).
+  const bf16_t* kbase = tab.k[seq] + (size_t)g * D + dq;
+  const uint32_t* vbase = (const uint32_t*)(tab.v[seq] + (size_t)g * D) + lane % DP;
+  const int vg = lane / DP;
+  bf16x8_t kq[2][KST];
+  uint32_t vq[2][VPL];
+  auto issue = [&](int t, int set) {
+    const int s0 = ws + t * TS;
+    const int sk = min(s0 + hl, we - 1);
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int k = grp + i * NG;
-      vv[i] = k < nk ? vbase[(size_t)(s0 + k) * (kvd / 2)] : 0u;
+    for (int i = 0; i < KST; ++i) kq[set][i] = *(const bf16x8_t*)(kbase + (size_t)sk * kvd + 32 * i);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int sv = min(s0 + vg + NSG * j, we - 1);
+      vq[set][j] = vbase[(size_t)sv * (kvd / 2)];
     }
   };
-  issue(start);
 
-  const uint32_t* qsrc = (const uint32_t*)(q + ((size_t)rt * nq + (size_t)g * G) * D);
-  for (int i = tid; i < G * DP; i += 256) qs[i / DP][i % DP] = qsrc[i];
-  if (tid < G) { Ms[tid] = -INFINITY; Ls[tid] = 0.f; }
-
+  float mrun = -INFINITY, lrun = 0.f;  // head hl's running max and sum
   float o0[G], o1[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) { o0[h] = 0.f; o1[h] = 0.f; }
-  __syncthreads();
 
-  for (int s0 = start; s0 < end; s0 += SUB) {
-    const int nk = min(SUB, end - s0);
-    // scores: lanes 4k..4k+3 share slot k, each over D/4 dims
-    {
-      float s[G];
+  auto step = [&](int t, int set) {
+    bf16x8_t kf[KST];
+    uint32_t vv[VPL];
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[h] = 0.f;
-      if (kslot < nk) {
+    for (int i = 0; i < KST; ++i) kf[i] = kq[set][i];
 #pragma unroll
-        for (int j = 0; j < DQ / 8; ++j) {
-          const u32x4_t kv = kreg[j];
+    for (int j = 0; j < VPL; ++j) vv[j] = vq[set][j];
+    issue(t + 2, set);
+    const int s0 = ws + t * TS;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const u32x4_t qv = *(const u32x4_t*)&qs[h][qq * (DQ / 2) + 4 * j];
-            float t = s[h];
-            t = dot2(qv.x, kv.x, t);
-            t = dot2(qv.y, kv.y, t);
-            t = dot2(qv.z, kv.z, t);
-            t = dot2(qv.w, kv.w, t);
-            s[h] = t;
-          }
-        }
-      }
+    for (int i = 0; i < KST; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[i], qf[i], acc, 0, 0, 0);
+    // lane l: head hl, slots s0 + 4(l/16) + j
+    float sc[4], mt = -INFINITY;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float t = s[h];
-        t += __shfl_xor(t, 1, WAVE);
-        t += __shfl_xor(t, 2, WAVE);
-        if (qq == 0) S[h][kslot] = kslot < nk ? t * scale : -INFINITY;
-      }
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = s0 + 4 * (lane >> 4) + j < we ? acc[j] * scale : -INFINITY;
+      mt = fmaxf(mt, sc[j]);
     }
-    __syncthreads();
-    // online softmax per head: one wave per head, lane = slot
-    for (int h = wave; h < G; h += 4) {
-      float v = S[h][lane];
-      float mt = wave_max(v);
-      float mold = Ms[h];
-      float mnew = fmaxf(mold, mt);
-      float e = lane < nk ? expf(v - mnew) : 0.f;
-      S[h][lane] = e;
-      float lt = wave_sum(e);
-      if (lane == 0) {
-        float a = expf(mold - mnew);  // 0 on the first sub-block (mold = -inf)
-        As[h] = a;
-        Ls[h] = Ls[h] * a + lt;
-        Ms[h] = mnew;
-      }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
+    const float mnew = fmaxf(mrun, mt);
+    const float alpha = expf(mrun - mnew);  // 0 on the first tile (mrun = -inf)
+    float e[4], lt = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = expf(sc[j] - mnew);
+      lt += e[j];
     }
-    __syncthreads();
-    // o = o * alpha + sum_k e_k v_k over this sub-block's slots grp, grp+NG, ...
+    lt += __shfl_xor(lt, 16, WAVE);
+    lt += __shfl_xor(lt, 32, WAVE);
+    lrun = lrun * alpha + lt;
+    mrun = mnew;
+    // o = o * alpha + sum over the tile's slots of e v (weights from lane
+    // h + 16(u/4), register u%4, for slot u)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      o0[h] *= As[h];
-      o1[h] *= As[h];
+      const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+      o0[h] *= a;
+      o1[h] *= a;
     }
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int k = grp + i * NG;
-      if (k >= nk) break;
-      const float v0 = bf_lo(vv[i]), v1 = bf_hi(vv[i]);
+    for (int j = 0; j < VPL; ++j) {
+      const float v0 = bf_lo(vv[j]), v1 = bf_hi(vv[j]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float e = S[h][k];
-        o0[h] = fmaf(e, v0, o0[h]);
-        o1[h] = fmaf(e, v1, o1[h]);
+        float w;
+        if (NSG == 1) {
+          w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e[j % 4]), h + 16 * (j / 4)));
+        } else {  // lanes of slot group vg take slot vg + 2j
+          const int u0 = 2 * j, u1 = 2 * j + 1;
+          const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e[u0 % 4]), h + 16 * (u0 / 4)));
+          const float w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e[u1 % 4]), h + 16 * (u1 / 4)));
+          w = vg ? w1 : w0;
+        }
+        o0[h] = fmaf(w, v0, o0[h]);
+        o1[h] = fmaf(w, v1, o1[h]);
       }
     }
-    if (s0 + SUB < end) issue(s0 + SUB);
-    __syncthreads();  // S is rewritten by the next sub-block
+  };
+  if (ntile > 0) {
+    issue(0, 0);
+    issue(1, 1);
+    int t = 0;
+    for (; t + 1 < ntile; t += 2) {
+      step(t, 0);
+      step(t + 1, 1);
+    }
+    if (t < ntile) step(t, 0);
   }
-
+  // the two slot groups' sums (d = 64), in group order
+  if (NSG == 2) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    O[grp][h][2 * dp] = o0[h];
-    O[grp][h][2 * dp + 1] = o1[h];
+    for (int h = 0; h < G; ++h) {
+      const float a0 = __shfl_xor(o0[h], 32, WAVE), a1 = __shfl_xor(o1[h], 32, WAVE);
+      if (vg == 0) { o0[h] += a0; o1[h] += a1; }
+    }
+  }
+  if (lane < G) {
+    sm[wave][lane] = mrun;
+    sl[wave][lane] = lrun;
+  }
+  if (vg == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      so[wave][h][2 * (lane % DP)] = o0[h];
+      so[wave][h][2 * (lane % DP) + 1] = o1[h];
+    }
   }
   __syncthreads();
-  for (int i = tid; i < G * (D + 2); i += 256) {
+  // the block's partial: its quarters combined in order (an empty quarter has
+  // max -inf and adds nothing; quarter 0 always holds the block's first slot)
+  for (int i = threadIdx.x; i < G * (D + 2); i += 256) {
     const int h = i / (D + 2), j = i % (D + 2);
-    float val;
-    if (j == 0) val = Ms[h];
-    else if (j == 1) val = Ls[h];
-    else {
-      val = 0.f;
+    float M = sm[0][h];
 #pragma unroll
-      for (int gi = 0; gi < NG; ++gi) val += O[gi][h][j - 2];
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][h]);
+    float val = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = expf(sm[w][h] - M);
+      val += f * (j == 0 ? 0.f : j == 1 ? sl[w][h] : so[w][h][j - 2]);
     }
+    if (j == 0) val = M;
     part[(((size_t)rt * nq + (size_t)g * G + h) * MAXB + b) * (D + 2) + j] = val;
   }
-
 }
 
 template <int D>

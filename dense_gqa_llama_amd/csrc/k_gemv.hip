@@ -42,6 +42,41 @@ struct GemvArgs {
 
 __device__ __forceinline__ float silu_bf16(float g) { return rbf(g / (1.0f + expf(-g))); }
 
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
+// Sums over the 64 lanes of NG groups of KG partials (v[g][k]), scattered:
+// afterwards v[0][0..KG-1] holds the sums of group lane >> (6 - log2 NG).
+// Each exchange halves the groups a lane carries (it keeps one half and adds
+// its partner's copy of it), lane bits 32, 16, 8, ... in turn, then the rest
+// of the butterfly runs on the kept group: every sum is associated exactly as
+// wave_sum's (xor 32, 16, 8, 4, 2, 1), own partial first, with NG - 1 + 6 -
+// log2 NG exchanges per partial instead of 6 NG.
+template <int NG, int KG>
+__device__ __forceinline__ void reduce_scatter(float (&v)[NG][KG], int lane) {
+  constexpr int K = ilog2(NG);
+  static_assert((1 << K) == NG && K <= 6, "power-of-two group count up to 64");
+#pragma unroll
+  for (int t = 0; t < K; ++t) {
+    const int m = 32 >> t;
+    const int half = (NG >> t) / 2;
+    const bool up = lane & m;
+#pragma unroll
+    for (int j = 0; j < NG / 2; ++j) {
+      if (j >= half) break;
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        const float lo = v[j][k], hi = v[j + half][k];
+        const float keep = up ? hi : lo, send = up ? lo : hi;
+        v[j][k] = keep + __shfl_xor(send, m, WAVE);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 32 >> K; m >= 1; m >>= 1)
+#pragma unroll
+    for (int k = 0; k < KG; ++k) v[0][k] += __shfl_xor(v[0][k], m, WAVE);
+}
+
 // NR weight rows per wave; for SWIGLU the first NR/2 come from the gate
 // matrix and the last NR/2 from the up matrix, for the same output columns.
 template <int R, int NR, int EPI, bool NORM, int P>
@@ -196,22 +231,26 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < NR; ++i)
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[i][r] = wave_sum(acc[i][r]);
-
+  // Lane sums, scattered so that one lane holds each output's sums (rows
+  // padded to a power of two with zeros), then one store per lane.
+  constexpr int RP = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : R <= 8 ? 8 : 16;
   if (EPI == GEMV_QKV_ROPE) {
-    // lane r rotates and stores row r's four outputs
+    // one group per row: its four outputs (two rotation pairs) in one lane
+    float v[RP][4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (lane != r) continue;
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[r][k] = r < R ? acc[k][r] : 0.f;
+    reduce_scatter<RP, 4>(v, lane);
+    constexpr int SH = 6 - ilog2(RP);
+    const int r = lane >> SH;
+    if (r < R && (lane & ((1 << SH) - 1)) == 0) {
       const int rt = a.row0 + r;
       const int seq = rt / a.tab.rows_per_seq;
       const int p = a.tab.pos0[seq] + rt % a.tab.rows_per_seq;
       const int half = a.d >> 1, kvd = a.nkv * a.d;
-      const float x0 = rbf(acc[0][r]), x1 = rbf(acc[1][r]);
-      const float y0 = rbf(acc[2][r]), y1 = rbf(acc[3][r]);
+      const float x0 = rbf(v[0][0]), x1 = rbf(v[0][1]);
+      const float y0 = rbf(v[0][2]), y1 = rbf(v[0][3]);
       bf16_t* dst;
       if (head >= a.nq + a.nkv) {  // values: no rotation
         dst = a.tab.v[seq] + (size_t)p * kvd + (head - a.nq - a.nkv) * a.d + i0;
@@ -232,23 +271,31 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     return;
   }
 
-  // Spread the stores over lanes: lane (c*R + r) writes column c of row r.
+  // one group per (column c, row r): for SWIGLU the gate and up sums
+  constexpr int KG = EPI == GEMV_SWIGLU ? 2 : 1;
+  constexpr int NG = COLS * RP;
+  float v[NG][KG];
 #pragma unroll
-  for (int c = 0; c < COLS; ++c) {
+  for (int c = 0; c < COLS; ++c)
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (lane != (c * R + r) % WAVE) continue;
-      const int n = n0 + c;
-      if (EPI == GEMV_STORE) {
-        a.out[(size_t)r * a.ldo + n] = f2bf(acc[c][r]);
-        if (a.out32) a.out32[(size_t)r * a.ld32 + n] = acc[c][r];
-      } else if (EPI == GEMV_RESIDUAL) {
-        bf16_t* h = a.out + (size_t)r * a.ldo + n;
-        *h = f2bf(bf2f(*h) + rbf(acc[c][r]));
-      } else {
-        float g = rbf(acc[c][r]), u = rbf(acc[c + COLS][r]);
-        a.out[(size_t)r * a.ldo + n] = f2bf(silu_bf16(g) * u);
-      }
+    for (int r = 0; r < RP; ++r) {
+      v[c * RP + r][0] = r < R ? acc[c][r] : 0.f;
+      if (KG == 2) v[c * RP + r][KG - 1] = r < R ? acc[c + COLS][r] : 0.f;
+    }
+  reduce_scatter<NG, KG>(v, lane);
+  constexpr int SH = 6 - ilog2(NG);
+  const int gi = lane >> SH, c = gi / RP, r = gi % RP;
+  if (r < R && (lane & ((1 << SH) - 1)) == 0) {
+    const int n = n0 + c;
+    if (EPI == GEMV_STORE) {
+      a.out[(size_t)r * a.ldo + n] = f2bf(v[0][0]);
+      if (a.out32) a.out32[(size_t)r * a.ld32 + n] = v[0][0];
+    } else if (EPI == GEMV_RESIDUAL) {
+      bf16_t* h = a.out + (size_t)r * a.ldo + n;
+      *h = f2bf(bf2f(*h) + rbf(v[0][0]));
+    } else {
+      float g = rbf(v[0][0]), u = rbf(v[0][KG - 1]);
+      a.out[(size_t)r * a.ldo + n] = f2bf(silu_bf16(g) * u);
     }
   }
 }
@@ -257,7 +304,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 // normalised windows up to GEMV_NORM_WHOLE_BYTES; otherwise chunks of at most
 // 32 KB (a multiple of the loop step).
 constexpr int GEMV_XLDS_BYTES = 64 * 1024;
-constexpr int GEMV_XCHUNK_BYTES = 32 * 1024;
+#ifndef GEMV_XCHUNK_BYTES
+#define GEMV_XCHUNK_BYTES (32 * 1024)
+#endif
 #ifndef GEMV_NORM_WHOLE_BYTES
 #define GEMV_NORM_WHOLE_BYTES (32 * 1024)
 #endif

@@ -223,15 +223,15 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
   float ob[MAXB];
 #pragma unroll
   for (int b = 0; b < MAXB; ++b) ob[b] = b < nb ? pp[(size_t)b * (D + 2) + 2 + j] : 0.f;
-  if (j < nb) {
-    wts[j] = pp[(size_t)j * (D + 2)];
-    lsum[j] = pp[(size_t)j * (D + 2) + 1];
+  for (int b = j; b < nb; b += D) {
+    wts[b] = pp[(size_t)b * (D + 2)];
+    lsum[b] = pp[(size_t)b * (D + 2) + 1];
   }
   __syncthreads();
   float M = -INFINITY;
   for (int b = 0; b < nb; ++b) M = fmaxf(M, wts[b]);
   __syncthreads();
-  if (j < nb) wts[j] = expf(wts[j] - M);
+  for (int b = j; b < nb; b += D) wts[b] = expf(wts[b] - M);
   __syncthreads();
   float L = 0.f, O = 0.f;
 #pragma unroll

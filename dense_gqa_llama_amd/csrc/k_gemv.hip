@@ -304,12 +304,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 // normalised windows up to GEMV_NORM_WHOLE_BYTES; otherwise chunks of at most
 // 32 KB (a multiple of the loop step).
 constexpr int GEMV_XLDS_BYTES = 64 * 1024;
-#ifndef GEMV_XCHUNK_BYTES
-#define GEMV_XCHUNK_BYTES (32 * 1024)
-#endif
-#ifndef GEMV_NORM_WHOLE_BYTES
-#define GEMV_NORM_WHOLE_BYTES (32 * 1024)
-#endif
+constexpr int GEMV_XCHUNK_BYTES = 32 * 1024;
+constexpr int GEMV_NORM_WHOLE_BYTES = 32 * 1024;
 
 template <int R, int EPI, bool NORM>
 static void launch_r(GemvArgs a, int N, hipStream_t s) {

@@ -2,6 +2,7 @@
 from the synthetic generator, running single block executions on the
 oracle's own inputs, and moving bf16 bits between torch and numpy."""
 import dataclasses
+import os
 import sys
 
 import numpy as np
@@ -12,9 +13,24 @@ from tests import parity
 KINDS = ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down")
 
 
+_PROGRESS = []
+
+
 def log(msg):
+    """Prints a progress line and appends it to gpurun_out/gpu_tests_progress.log
+    (pytest holds a test's own output until it ends; the file shows a long test
+    advancing while it runs)."""
     print(msg, flush=True)
     sys.stdout.flush()
+    try:
+        if not _PROGRESS:
+            d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+            os.makedirs(d, exist_ok=True)
+            _PROGRESS.append(open(os.path.join(d, "gpu_tests_progress.log"), "a"))
+        _PROGRESS[0].write(msg + "\n")
+        _PROGRESS[0].flush()
+    except OSError:
+        pass
 
 
 def u16(t):

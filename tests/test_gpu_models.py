@@ -72,13 +72,15 @@ def _run(cfg, sampled_execs):
     oseq = om.new_sequence(SAMPLE_ROWS + DECODE)
     r = om.forward(oseq, tokens=ptoks[:SAMPLE_ROWS], logits="all", capture=True)
     ref64, refb, caps, h_out = r["logits64"], r["logits"], r["capture"], r["h_out"]
+    log(f"config {cfg}: oracle prompt rows done")
     gen = [int(r["tokens"][-1])]
     dec64, decb = [], []
-    for _ in range(DECODE):
+    for i in range(DECODE):
         rr = om.forward(oseq, tokens=np.array([gen[-1]], dtype=np.int32), logits="all")
         dec64.append(rr["logits64"][0])
         decb.append(rr["logits"][0])
         gen.append(int(rr["tokens"][-1]))
+        log(f"config {cfg}: oracle decode step {i + 1}/{DECODE} done")
     log(f"config {cfg}: oracle greedy {gen}")
     # the model's own noise floor: the same rows with every element of the
     # first row's embedding moved by one bf16 step (a rounding-scale change)
@@ -92,8 +94,10 @@ def _run(cfg, sampled_execs):
     om2 = OracleModel(g, Nudged())
     s2o = om2.new_sequence(SAMPLE_ROWS + DECODE)
     n64 = [om2.forward(s2o, tokens=ptoks[:SAMPLE_ROWS], logits="all")["logits64"]]
-    for t in gen[:DECODE]:
+    log(f"config {cfg}: nudged oracle prompt rows done")
+    for i, t in enumerate(gen[:DECODE]):
         n64.append(om2.forward(s2o, tokens=np.array([t], dtype=np.int32), logits="all")["logits64"])
+        log(f"config {cfg}: nudged oracle step {i + 1}/{DECODE} done")
     n64 = np.concatenate(n64)
     w = sd.weights(g)
     torch.cuda.synchronize()

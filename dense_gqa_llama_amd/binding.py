@@ -73,6 +73,9 @@ _SIGS = {
                                     ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
     "llama_draft_round": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P,
                                           ctypes.POINTER(ctypes.c_int32), _P]),
+    "llama_draft_round_sampled": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P,
+                                                  ctypes.c_float, ctypes.c_int32, ctypes.c_float,
+                                                  _P, _P, ctypes.POINTER(ctypes.c_int32), _P]),
     "llama_set_timing": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32]),
     "llama_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_double),
                                          ctypes.POINTER(ctypes.c_int64)]),
@@ -201,6 +204,16 @@ def llama_draft_round(target, target_kv, draft, draft_kv, n_draft, last_token, t
     n = ctypes.c_int32(0)
     _check(lib.llama_draft_round(target, target_kv, draft, draft_kv, n_draft, last_token,
                                  tokens_out, ctypes.byref(n), stream))
+    return n.value
+
+
+def llama_draft_round_sampled(target, target_kv, draft, draft_kv, n_draft, last_token,
+                              temperature, top_k, top_p, u, tokens_out, stream=None):
+    """Returns the number of tokens the round wrote to tokens_out."""
+    n = ctypes.c_int32(0)
+    _check(lib.llama_draft_round_sampled(target, target_kv, draft, draft_kv, n_draft, last_token,
+                                         temperature, top_k, top_p, u, tokens_out,
+                                         ctypes.byref(n), stream))
     return n.value
 
 

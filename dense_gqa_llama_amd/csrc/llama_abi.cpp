@@ -565,9 +565,35 @@ int llama_decode_step(llama_model* m, llama_kv* const* kvs, int32_t n_seq,
   return LLAMA_OK;
 }
 
-int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* draft,
-                      llama_kv* draft_kv, int32_t n_draft, const int32_t* last_token_dev,
-                      int32_t* tokens_out_dev, int32_t* n_out, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+struct DraftSampling {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  const float* u;
+};
+
+int check_sampling(const llama_model* m, float temperature, int32_t top_k, float top_p) {
+  const int V = m->d.V;
+  if (!(temperature > 0.0f) || !(temperature < INFINITY))
+    return fail(LLAMA_E_ARG, "temperature must be positive and finite (greedy draws take "
+                "next_tokens in the step calls)");
+  if (top_k < 1 || top_k > LLAMA_SAMPLE_MAX_TOP_K || top_k > V)
+    return fail(LLAMA_E_ARG, "top_k %d outside 1..%d", top_k, std::min(LLAMA_SAMPLE_MAX_TOP_K, V));
+  if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return fail(LLAMA_E_ARG, "top_p must lie in (0, 1]");
+  if (sample_chunks(V) * top_k > 4096)
+    return fail(LLAMA_E_ARG, "top_k %d too large for a vocabulary of %d", top_k, V);
+  return LLAMA_OK;
+}
+
+// One drafted round; sp == NULL: the target's greedy tokens, else its
+// seeded draws (sp->u[i] for the token after window row i).
+int draft_round(llama_model* target, llama_kv* target_kv, llama_model* draft, llama_kv* draft_kv,
+                int32_t n_draft, const int32_t* last_token_dev, const DraftSampling* sp,
+                int32_t* tokens_out_dev, int32_t* n_out, void* hip_stream) {
   if (!target || !draft) return fail(LLAMA_E_ARG, "model is NULL");
   if (target == draft) return fail(LLAMA_E_ARG, "the draft model is the target model");
   int rc = check_kv(target, target_kv);
@@ -580,6 +606,11 @@ int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* dra
   if (n_draft < 1 || n_draft + 1 > target->cfg.max_window_rows)
     return fail(LLAMA_E_ARG, "n_draft %d outside 1..%d (the target's window less one)", n_draft,
                 target->cfg.max_window_rows - 1);
+  if (sp) {
+    if (!sp->u) return fail(LLAMA_E_ARG, "uniforms are NULL");
+    rc = check_sampling(target, sp->temperature, sp->top_k, sp->top_p);
+    if (rc) return rc;
+  }
   const int p = target_kv->length;
   if (draft_kv->length != p)
     return fail(LLAMA_E_POSITION, "the draft cache holds %d positions, the target's %d",
@@ -596,7 +627,7 @@ int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* dra
   if (rc) return rc;
   hipStream_t s = (hipStream_t)hip_stream;
   int32_t* win = target->at<int32_t>(target->L.draft);  // [0..k]: last, d_1 .. d_k
-  int32_t* tt = win + 32;                                 // target's greedy tokens
+  int32_t* tt = win + 32;                                 // the target's tokens
   int32_t* cnt = win + 64;
   if (hipMemcpyAsync(win, last_token_dev, 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return dev_check("drafted round copy");
@@ -607,9 +638,19 @@ int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* dra
     if (rc) return rc;
   }
   // the target's verdict on all of them in one window
-  rc = llama_decode_step(target, &target_kv, 1, win, nullptr, n_draft + 1, nullptr, nullptr,
-                         nullptr, tt, s);
-  if (rc) return rc;
+  if (!sp) {
+    rc = llama_decode_step(target, &target_kv, 1, win, nullptr, n_draft + 1, nullptr, nullptr,
+                           nullptr, tt, s);
+    if (rc) return rc;
+  } else {
+    void* lg = target->ws + target->L.logits;  // room for max(16, decode rows) rows
+    rc = llama_decode_step(target, &target_kv, 1, win, nullptr, n_draft + 1, nullptr, lg, nullptr,
+                           nullptr, s);
+    if (rc) return rc;
+    launch_sample(lg, target->d.V, target->d.V, n_draft + 1, sp->top_k, sp->temperature, sp->top_p,
+                  sp->u, target->at<float>(target->L.smp_v), target->at<int>(target->L.smp_i),
+                  target->at<int>(target->L.smp_bad), tt, target->at<int>(target->L.flag), s);
+  }
   launch_draft_accept(win, tt, n_draft, tokens_out_dev, cnt, s);
   rc = dev_check("drafted round acceptance");
   if (rc) return rc;
@@ -631,6 +672,26 @@ int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* dra
   return LLAMA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* draft,
+                      llama_kv* draft_kv, int32_t n_draft, const int32_t* last_token_dev,
+                      int32_t* tokens_out_dev, int32_t* n_out, void* hip_stream) {
+  return draft_round(target, target_kv, draft, draft_kv, n_draft, last_token_dev, nullptr,
+                     tokens_out_dev, n_out, hip_stream);
+}
+
+int llama_draft_round_sampled(llama_model* target, llama_kv* target_kv, llama_model* draft,
+                              llama_kv* draft_kv, int32_t n_draft, const int32_t* last_token_dev,
+                              float temperature, int32_t top_k, float top_p, const float* u_dev,
+                              int32_t* tokens_out_dev, int32_t* n_out, void* hip_stream) {
+  const DraftSampling sp{temperature, top_k, top_p, u_dev};
+  return draft_round(target, target_kv, draft, draft_kv, n_draft, last_token_dev, &sp,
+                     tokens_out_dev, n_out, hip_stream);
+}
+
 int llama_sample(llama_model* m, const void* logits_bf16_dev, int32_t rows, int64_t ld,
                  float temperature, int32_t top_k, float top_p, const float* u_dev,
                  int32_t* tokens_dev, void* hip_stream) {
@@ -641,14 +702,8 @@ int llama_sample(llama_model* m, const void* logits_bf16_dev, int32_t rows, int6
   if (rows < 1 || rows > LLAMA_SAMPLE_MAX_ROWS)
     return fail(LLAMA_E_ARG, "rows %d outside 1..%d", rows, LLAMA_SAMPLE_MAX_ROWS);
   if (ld < V) return fail(LLAMA_E_ARG, "row stride %lld below the vocabulary %d", (long long)ld, V);
-  if (!(temperature > 0.0f) || !(temperature < INFINITY))
-    return fail(LLAMA_E_ARG, "temperature must be positive and finite (greedy draws take "
-                "next_tokens in the step calls)");
-  if (top_k < 1 || top_k > LLAMA_SAMPLE_MAX_TOP_K || top_k > V)
-    return fail(LLAMA_E_ARG, "top_k %d outside 1..%d", top_k, std::min(LLAMA_SAMPLE_MAX_TOP_K, V));
-  if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return fail(LLAMA_E_ARG, "top_p must lie in (0, 1]");
-  if (sample_chunks(V) * top_k > 4096)
-    return fail(LLAMA_E_ARG, "top_k %d too large for a vocabulary of %d", top_k, V);
+  int rc = check_sampling(m, temperature, top_k, top_p);
+  if (rc) return rc;
   hipStream_t s = (hipStream_t)hip_stream;
   ready_flag(m, s);
   launch_sample(logits_bf16_dev, V, ld, rows, top_k, temperature, top_p, u_dev,

@@ -122,6 +122,19 @@ class Model:
                                 int(n_draft), last_token.data_ptr(), out.data_ptr(), _stream())
         return out, n
 
+    def draft_round_sampled(self, seq, draft, draft_seq, n_draft, last_token, u, temperature,
+                            top_k, top_p, out=None):
+        """As draft_round, with this model's tokens drawn by seeded sampling:
+        u (float32 [n_draft + 1] on the device) holds the uniform of each
+        window row's draw."""
+        if out is None:
+            out = torch.empty(n_draft + 1, dtype=torch.int32, device=last_token.device)
+        n = B.llama_draft_round_sampled(self.handle, seq.handle, draft.handle, draft_seq.handle,
+                                        int(n_draft), last_token.data_ptr(), float(temperature),
+                                        int(top_k), float(top_p), u.data_ptr(), out.data_ptr(),
+                                        _stream())
+        return out, n
+
     def check_finite(self):
         B.llama_check_finite(self.handle, _stream())
 

@@ -230,6 +230,22 @@ int llama_draft_round(llama_model* target, llama_kv* target_kv, llama_model* dra
                       llama_kv* draft_kv, int32_t n_draft, const int32_t* last_token_dev,
                       int32_t* tokens_out_dev, int32_t* n_out, void* hip_stream);
 
+/* The same round with seeded sampling (model card "Nanbeige4.3-33B EXL3",
+ * section on its draft model: the target samples and accepts matching draft
+ * tokens, so the output follows the target's own sampling).  The draft still
+ * proposes its greedy tokens; the target draws its token after each window
+ * row i with llama_sample's rule (temperature, top_k, top_p) against u_dev[i]
+ * (n_draft + 1 floats in [0, 1), device), and the round keeps the leading
+ * proposals equal to those draws, then the target's own draw after them.
+ * With u_dev[i] the uniform of position p + i, the reply equals seeded
+ * sampling by plain steps with the same uniforms, whatever the draft
+ * proposes.  Sampling arguments as llama_sample; the rest as
+ * llama_draft_round. */
+int llama_draft_round_sampled(llama_model* target, llama_kv* target_kv, llama_model* draft,
+                              llama_kv* draft_kv, int32_t n_draft, const int32_t* last_token_dev,
+                              float temperature, int32_t top_k, float top_p, const float* u_dev,
+                              int32_t* tokens_out_dev, int32_t* n_out, void* hip_stream);
+
 /* Synchronises hip_stream, then reports LLAMA_E_NONFINITE if any greedy or
  * sampled draw since the last call met a non-finite logit row (and clears
  * the flag), else LLAMA_OK. */

@@ -187,9 +187,10 @@ def test_sampling_refusals():
 
 
 def test_draft_round_refusals():
-    """llama_draft_round checks both models and caches before it enqueues
-    anything: same vocabulary, a window that fits, caches of equal length
-    with room for the round, and refusals leave the lengths as they were."""
+    """llama_draft_round (and its seeded variant) checks both models and
+    caches before it enqueues anything: same vocabulary, a window that fits,
+    caches of equal length with room for the round, sampling arguments, and
+    refusals leave the lengths as they were."""
     g = CONFIGS[1]
     t, _ = load(g, max_chunk_rows=64, max_window_rows=8)
     d, _ = load(g, max_chunk_rows=64, max_window_rows=1)
@@ -211,6 +212,16 @@ def test_draft_round_refusals():
         B.llama_kv_set_length(tkv, 27)
         B.llama_kv_set_length(dkv, 27)
         expect(B.LLAMA_E_CAPACITY, call, n=5)  # the draft cache ends at 32
+        # the seeded variant also checks its sampling arguments
+        B.llama_kv_set_length(dkv, 27)
+        B.llama_kv_set_length(tkv, 27)
+
+        def sampled(T=0.6, K=20, P=0.95, u=FAKE, n=4):
+            return B.llama_draft_round_sampled(t, tkv, d, dkv, n, FAKE, T, K, P, u, FAKE)
+        for kw in (dict(T=0.0), dict(T=float("inf")), dict(K=0), dict(K=65), dict(P=0.0),
+                   dict(P=1.5), dict(u=None), dict(n=8)):
+            expect(B.LLAMA_E_ARG, sampled, **kw)
+        expect(B.LLAMA_E_CAPACITY, sampled, n=5)
         dkv2 = B.llama_kv_alloc(d, 128, FAKE, B.llama_kv_bytes(d, 128))
         B.llama_kv_set_length(tkv, 60)
         B.llama_kv_set_length(dkv2, 60)

@@ -97,3 +97,60 @@ def test_drafted_greedy_equals_plain_greedy(kind):
         assert all(a == k for a, k in taken)
     if kind == "lm_head_quarter":
         assert 0 < rate < 1
+
+
+def _plain_sampled(model, p, n, u, T, K, P):
+    s = model.new_sequence(CAP)
+    lg = model.prefill(s, tokens=to_dev(p))["logits"]
+    toks = []
+    for i in range(n):
+        t = model.sample(lg, u[i:i + 1], T, K, P)
+        toks.append(int(t.item()))
+        if i + 1 < n:
+            lg = model.decode([s], tokens=t)["logits"]
+    return toks, s
+
+
+def _drafted_sampled(target, draft, p, n, u, T, K, P):
+    ts, ds = target.new_sequence(CAP), draft.new_sequence(CAP)
+    lg = target.prefill(ts, tokens=to_dev(p))["logits"]
+    draft.prefill(ds, tokens=to_dev(p), want_logits=False)
+    last = target.sample(lg, u[0:1], T, K, P)
+    out, taken, i = [int(last.item())], [], 0
+    while len(out) < n:
+        k = SCHEDULE[i % len(SCHEDULE)]
+        i += 1
+        j = len(out)  # the round's draws take uniforms j .. j + k
+        toks, m = target.draft_round_sampled(ts, draft, ds, k, last, u[j:j + k + 1], T, K, P)
+        assert ts.length == ds.length
+        out += toks[:m].cpu().numpy().tolist()
+        taken.append((m - 1, k))
+        last = toks[m - 1:m].clone()
+    return out, ts, taken
+
+
+@pytest.mark.parametrize("kind", ["self", "lm_head_quarter"])
+def test_drafted_sampling_equals_plain_sampling(kind):
+    """Seeded sampling by drafted rounds (the target draws each window row's
+    token with that position's uniform and keeps matching proposals) equals
+    seeded sampling by plain steps with the same uniforms."""
+    from synth import device as sd
+    g = config(1)
+    w = sd.weights(g)
+    target = gpu_model(g, CAP, max_chunk_rows=64, max_window_rows=16, max_seqs=1, weights=w)
+    draft = gpu_model(g, CAP, max_chunk_rows=64, max_window_rows=1, max_seqs=1,
+                      weights=_draft_weights(kind, g, w))
+    p = prompt(g, n=g.prompt_len)
+    T, K, P = 0.6, 20, 0.95
+    u = sd.uniform(N_TOKENS + 16, 4800, TensorIds.SAMPLE_UNIFORM)
+    want, ps = _plain_sampled(target, p, N_TOKENS, u, T, K, P)
+    got, ts, taken = _drafted_sampled(target, draft, p, N_TOKENS, u, T, K, P)
+    target.check_finite()
+    draft.check_finite()
+    rate = sum(a for a, _ in taken) / max(1, sum(k for _, k in taken))
+    log(f"sampled, draft {kind}: {len(taken)} rounds, proposals taken {rate:.2f}, {taken}")
+    assert got[:N_TOKENS] == want
+    n = min(ts.length, ps.length)
+    assert n >= len(p) + N_TOKENS - 1
+    assert np.array_equal(u16(ts.view())[:, :, :n], u16(ps.view())[:, :, :n])
+    assert 0 < rate < 1

@@ -5,10 +5,12 @@
 // the matrix units).
 //
 // Both operands are K-contiguous: activations [M][K] and published weights
-// [N][K].  Every output is a chain of v_mfma_f32_32x32x16_bf16 over 16-deep k
-// steps in increasing k: lane l of an MFMA reads row l%32 and 8 consecutive k
-// at 8*(l/32) of each operand, and holds output rows 8*(j/4) + 4*(l/32) + j%4
-// of column l%32 in its accumulators.  Two kernels share that order, so every
+// [N][K].  Every output is a chain of v_mfma_f32_16x16x32_bf16 over 32-deep k
+// steps in increasing k: lane l of an MFMA reads row l%16 and 8 consecutive k
+// at 8*(l/16) of each operand, and holds output rows 4*(l/16) + j of column
+// l%16 in its four accumulators.  (The 16x16x32 form sustains a higher
+// product rate on gfx950 than 32x32x16 at the same fragment traffic per
+// product when each wave keeps the same sub-tile.)  Two kernels share that order, so every
 // output's bits are the same whichever runs and whatever M is:
 // gemm_alt_kernel (256 x 256 tiles, an alternating two-group schedule with
 // LDS-direct operand copies) and gemm_kernel (smaller tiles, register-staged
@@ -17,7 +19,8 @@
 // Epilogues: STORE (bf16 and optionally the fp32 sum), RESIDUAL
 // (h = bf16(h + bf16(acc))) and SWIGLU: the tile's columns alternate 32 gate
 // rows and the same 32 up rows of the weights, so one wave holds g and u of
-// the same outputs and writes bf16(bf16(silu(bf16(g))) * bf16(u)).
+// the same outputs (16-column MFMA tiles j and j + 2 of each 64-column group)
+// and writes bf16(bf16(silu(bf16(g))) * bf16(u)).
 #include "common.h"
 #include "launch.h"
 
@@ -40,30 +43,31 @@ struct GemmArgs {
 
 __device__ __forceinline__ float silu_r(float g) { return rbf(g / (1.0f + expf(-g))); }
 
-// Epilogue of a wave's TM x TN 32x32 tiles at rows r0.., tile columns c0..:
-// lane l holds column l%32 and rows 8*(j/4) + 4*(l/32) + j%4 of each.
+// Epilogue of a wave's TM x TN 16x16 tiles at rows r0.., tile columns c0..
+// (c0 a multiple of 64): lane l holds column l%16 and rows 4*(l/16) + r of each.
 template <int EPI, int TM, int TN>
-__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16_t (&acc)[TM][TN], int r0,
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4_t (&acc)[TM][TN], int r0,
                                            int c0, int lane) {
-  const int lr = lane & 31, hrow = (lane >> 5) * 4;
+  const int lc = lane & 15, hrow = (lane >> 4) * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = r0 + i * 32 + 8 * (r >> 2) + hrow + (r & 3);
+    for (int r = 0; r < 4; ++r) {
+      const int m = r0 + i * 16 + hrow + r;
       if (m >= a.M) continue;
       if (EPI == GEMV_SWIGLU) {
 #pragma unroll
-        for (int j = 0; j < TN; j += 2) {
-          const int col = c0 + j * 32;  // gate tile column; up follows at +32
-          const int n = (col >> 6) * 32 + lr;
-          float g = rbf(acc[i][j][r]), u = rbf(acc[i][j + 1][r]);
+        for (int j = 0; j < TN; ++j) {
+          if ((j & 3) >= 2) continue;  // up tiles, read with their gate tile
+          const int col = c0 + j * 16;  // gate tile column; up follows at +32
+          const int n = (col >> 6) * 32 + (col & 31) + lc;
+          float g = rbf(acc[i][j][r]), u = rbf(acc[i][j + 2][r]);
           a.out[(size_t)m * a.ldo + n] = f2bf(silu_r(g) * u);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int n = c0 + j * 32 + lr;
+          const int n = c0 + j * 16 + lc;
           const float v = acc[i][j][r];
           bf16_t* o = a.out + (size_t)m * a.ldo + n;
           if (EPI == GEMV_STORE) {
@@ -89,7 +93,7 @@ __device__ __forceinline__ int xcd_tile(int b, int nt) {
 
 // A BM x BN block tile staged through LDS in BK-deep slices, double-buffered
 // (rows padded to BK + 8 elements); each wave owns a WM x WN sub-tile of
-// 32x32 MFMA tiles.  Register budget: two waves per SIMD (two workgroups per
+// 16x16 MFMA tiles.  Register budget: two waves per SIMD (two workgroups per
 // CU when a workgroup has four waves).
 template <int BM, int BN, int WM, int WN, int EPI, int BK>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, (BM / WM) * (BN / WN) <= 4 ? 2 : 1)
@@ -98,10 +102,10 @@ void gemm_kernel(GemmArgs a, int mtiles) {
   constexpr int CPR = BK / 8;   // 16-byte chunks per tile row
   constexpr int NWN = BN / WN;
   constexpr int NT = (BM / WM) * NWN * 64;
-  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int A_LD = BM * CPR / NT, B_LD = BN * CPR / NT;  // 16-byte chunks per thread
   static_assert(A_LD * NT == BM * CPR && B_LD * NT == BN * CPR, "tile / thread mismatch");
-  static_assert(EPI != GEMV_SWIGLU || WN % 64 == 0, "SWIGLU pairs 32-column tiles");
+  static_assert(EPI != GEMV_SWIGLU || WN % 64 == 0, "SWIGLU pairs 32-column halves");
 
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   bf16_t* sA0 = smem;
@@ -140,13 +144,13 @@ void gemm_kernel(GemmArgs a, int mtiles) {
   }
   const int st_off = (tid / CPR) * LDK + (tid % CPR) * 8;  // chunk i: + i*(NT/CPR)*LDK
 
-  f32x16_t acc[TM][TN];
+  f32x4_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
   // Two register sets of staged global loads: the loads of k-tile kt + 2 are
   // issued while tile kt is consumed and tile kt + 1 waits in the other set,
@@ -171,9 +175,9 @@ void gemm_kernel(GemmArgs a, int mtiles) {
   };
 
   const int nk = a.K / BK;
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
   const int fa_off = (wm * WM + lr) * LDK + lk, fb_off = (wn * WN + lr) * LDK + lk;
-  constexpr int KS = BK / 16;       // MFMA steps per k-tile
+  constexpr int KS = BK / 32;       // MFMA steps per k-tile
   constexpr int NMF = TM * TN;      // MFMAs per step
   constexpr int NFR = TM + TN;      // fragment reads per step
   static_assert(NFR <= NMF, "one fragment read per product");
@@ -187,25 +191,25 @@ void gemm_kernel(GemmArgs a, int mtiles) {
     // Fragments of step ks + 1 are read while step ks's products run.
     bf16x8_t fa[2][TM], fb[2][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = *(const bf16x8_t*)&sA[i * 32 * LDK];
+    for (int i = 0; i < TM; ++i) fa[0][i] = *(const bf16x8_t*)&sA[i * 16 * LDK];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = *(const bf16x8_t*)&sB[j * 32 * LDK];
+    for (int j = 0; j < TN; ++j) fb[0][j] = *(const bf16x8_t*)&sB[j * 16 * LDK];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int cur = ks & 1;
       if (ks + 1 < KS) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          fa[cur ^ 1][i] = *(const bf16x8_t*)&sA[i * 32 * LDK + (ks + 1) * 16];
+          fa[cur ^ 1][i] = *(const bf16x8_t*)&sA[i * 16 * LDK + (ks + 1) * 32];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          fb[cur ^ 1][j] = *(const bf16x8_t*)&sB[j * 32 * LDK + (ks + 1) * 16];
+          fb[cur ^ 1][j] = *(const bf16x8_t*)&sB[j * 16 * LDK + (ks + 1) * 32];
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     }
     lstore(set ^ 1, buf ^ 1);
     // pinned order: the global loads first, the first step's fragment reads,
@@ -251,7 +255,7 @@ void gemm_kernel(GemmArgs a, int mtiles) {
 // ---------------------------------------------------------------------------
 // 256 x 256 tiles on an alternating schedule.  Eight waves, two per SIMD, in
 // two groups: group g (waves 4g .. 4g + 3, one per SIMD) owns output rows
-// 128g .. 128g + 127, each wave a 128 x 64 sub-tile.  Phases alternate: in one
+// 128g .. 128g + 127, each wave a 128 x 64 sub-tile (8 x 4 MFMA tiles).  Phases alternate: in one
 // a group's waves issue nothing but products of a whole 64-deep k-tile from
 // registers, while the other group's waves read their next k-tile's fragments
 // from LDS and issue the copies of a later k-tile; then the groups swap.  The
@@ -261,7 +265,8 @@ void gemm_kernel(GemmArgs a, int mtiles) {
 // Operand tiles go from global memory straight to LDS (16-byte LDS-direct
 // loads, one KiB = 8 rows of 128 bytes per copy), double-buffered: rows of
 // 64 k, chunk c of row r stored at chunk c ^ ((r >> 1) & 7), so a fragment
-// read (rows l%32, one chunk) touches every bank once per 16 lanes.  The
+// read (rows l%16, one chunk per 16 lanes) touches every bank once per 16
+// lanes.  The
 // copies of tile kt + 2 go into tile kt's buffer as soon as both groups have
 // read it: activation rows 0-127 (read by group 0 only) by group 1 while it
 // reads tile kt, the rest by group 0 in the next phase.  The products run in
@@ -287,7 +292,7 @@ __device__ __forceinline__ void wait_copies() {  // at most N of this wave's cop
 
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles) {
-  constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, TM = 4, TN = 2, KS = 4;
+  constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, TM = 8, TN = 4, KS = 2;
   constexpr int TILE = BM * BK * 2;  // bytes of one operand k-tile; LDS: A0 A1 B0 B1
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   uint8_t* lds = (uint8_t*)smem;
@@ -337,21 +342,21 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
     __builtin_amdgcn_global_load_lds((const void*)(b + go), (lds_ptr_t)(lds + loff), 16, 0, 0);
   };
 
-  f32x16_t acc[TM][TN];
+  f32x4_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
-  // fragment of a 32-row tile: lane l reads row l%32, logical chunk
-  // 2ks + l/32, stored at that ^ ((l%32 >> 1) & 7)
-  const int lr = lane & 31, swz = (lr >> 1) & 7;
+  // fragment of a 16-row tile: lane l reads row l%16, logical chunk
+  // 4ks + l/16, stored at that ^ ((l%16 >> 1) & 7)
+  const int lr = lane & 15, swz = (lr >> 1) & 7;
   uint32_t fa_off[KS], fb_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t ch = (uint32_t)(((2 * ks + (lane >> 5)) ^ swz) * 16);
+    const uint32_t ch = (uint32_t)(((4 * ks + (lane >> 4)) ^ swz) * 16);
     fa_off[ks] = (uint32_t)(grp * WM + lr) * 128 + ch;
     fb_off[ks] = 2 * TILE + (uint32_t)(q * WN + lr) * 128 + ch;
   }
@@ -361,9 +366,9 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[ks][i] = *(const bf16x8_t*)(lds + fa_off[ks] + bo + i * 32 * 128);
+      for (int i = 0; i < TM; ++i) fa[ks][i] = *(const bf16x8_t*)(lds + fa_off[ks] + bo + i * 16 * 128);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[ks][j] = *(const bf16x8_t*)(lds + fb_off[ks] + bo + j * 32 * 128);
+      for (int j = 0; j < TN; ++j) fb[ks][j] = *(const bf16x8_t*)(lds + fb_off[ks] + bo + j * 16 * 128);
     }
   };
   auto multiply = [&]() {
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0);
   };
 
   const int nk = a.K / BK;
@@ -475,7 +480,7 @@ static int cu_count() {
 // every weight segment starts at a multiple of 256 (SwiGLU always), unless
 // 256 x 128 tiles (eight waves of 64 x 64, about 0.72 the time of a 256 x 256
 // tile) would fill the CUs in fewer rounds' worth of time.  Other widths take
-// 128 x 128 tiles.  The split of K into 64-deep tiles and 16-deep MFMA steps,
+// 128 x 128 tiles.  The split of K into 64-deep tiles and 32-deep MFMA steps,
 // and so every output's bits, is the same for all of them.
 template <int EPI>
 static void launch_epi(GemmArgs a, int ncols, bool aligned, hipStream_t s) {

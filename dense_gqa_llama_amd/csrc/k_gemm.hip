@@ -12,7 +12,7 @@
 // product rate on gfx950 than 32x32x16 at the same fragment traffic per
 // product when each wave keeps the same sub-tile.)  Two kernels share that order, so every
 // output's bits are the same whichever runs and whatever M is:
-// gemm_alt_kernel (256 x 256 tiles, an alternating two-group schedule with
+// gemm_alt_kernel (256 x 256 or 256 x 224 tiles, an alternating two-group schedule with
 // LDS-direct operand copies) and gemm_kernel (smaller tiles, register-staged
 // copies, one pinned interleaved schedule).
 //
@@ -23,6 +23,8 @@
 // and writes bf16(bf16(silu(bf16(g))) * bf16(u)).
 #include "common.h"
 #include "launch.h"
+
+#include <algorithm>
 
 namespace {
 
@@ -253,24 +255,27 @@ void gemm_kernel(GemmArgs a, int mtiles) {
 }
 
 // ---------------------------------------------------------------------------
-// 256 x 256 tiles on an alternating schedule.  Eight waves, two per SIMD, in
-// two groups: group g (waves 4g .. 4g + 3, one per SIMD) owns output rows
-// 128g .. 128g + 127, each wave a 128 x 64 sub-tile (8 x 4 MFMA tiles).  Phases alternate: in one
-// a group's waves issue nothing but products of a whole 64-deep k-tile from
-// registers, while the other group's waves read their next k-tile's fragments
-// from LDS and issue the copies of a later k-tile; then the groups swap.  The
-// SIMD's matrix pipe is fed by one wave while its partner waits on memory, so
-// the LDS reads and copies stay off the products' path.
+// 256 x BN tiles (BN = 256 or 224) on an alternating schedule.  Eight waves,
+// two per SIMD, in two groups: group g (waves 4g .. 4g + 3, one per SIMD)
+// owns tile columns g*BN/2 .. (g+1)*BN/2 - 1, wave q of a group rows
+// 64q .. 64q + 63: a 64 x BN/2 sub-tile of 16x16 MFMA tiles.  Phases
+// alternate: in one a group's waves issue nothing but products of a whole
+// 64-deep k-tile from registers, while the other group's waves read their
+// next k-tile's fragments from LDS and issue the copies of a later k-tile;
+// then the groups swap.  The SIMD's matrix pipe is fed by one wave while its
+// partner waits on memory, so the LDS reads and copies stay off the products'
+// path.  BN = 224 puts 7,168-wide projections on exactly 256 tiles at
+// M = 2,048 (224 tiles of 256 would leave an eighth of the CUs idle).
 //
 // Operand tiles go from global memory straight to LDS (16-byte LDS-direct
 // loads, one KiB = 8 rows of 128 bytes per copy), double-buffered: rows of
 // 64 k, chunk c of row r stored at chunk c ^ ((r >> 1) & 7), so a fragment
 // read (rows l%16, one chunk per 16 lanes) touches every bank once per 16
-// lanes.  The
-// copies of tile kt + 2 go into tile kt's buffer as soon as both groups have
-// read it: activation rows 0-127 (read by group 0 only) by group 1 while it
-// reads tile kt, the rest by group 0 in the next phase.  The products run in
-// the same order as gemm_kernel's, so the two give the same bits.
+// lanes.  The copies of tile kt + 2 go into tile kt's buffer as soon as both
+// groups have read it: the weight rows of group 0's columns (read by group 0
+// only) by group 1 while it reads tile kt, the rest by group 0 in the next
+// phase.  The products run in the same order as gemm_kernel's, so the two
+// give the same bits.
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -285,15 +290,20 @@ __device__ __forceinline__ void phase_barrier() {
 
 template <int N>
 __device__ __forceinline__ void wait_copies() {  // at most N of this wave's copies in flight
+  static_assert(N == 0 || N == 3 || N == 4, "wait counts in use");
   __builtin_amdgcn_sched_barrier(0);
   if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
 }
 
-template <int EPI>
+template <int EPI, int BN>
 __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles) {
-  constexpr int BM = 256, BN = 256, BK = 64, WM = 128, WN = 64, TM = 8, TN = 4, KS = 2;
-  constexpr int TILE = BM * BK * 2;  // bytes of one operand k-tile; LDS: A0 A1 B0 B1
+  constexpr int BM = 256, BK = 64, WM = 64, WN = BN / 2, TM = WM / 16, TN = WN / 16, KS = 2;
+  constexpr int TILE = BM * BK * 2;  // bytes of an activation k-tile; LDS: A0 A1 B0 B1, TILE each
+  constexpr int NCB = BN / 8, NCB0 = NCB / 2;  // weight copies per k-tile; those of group 0's columns
+  static_assert(BN % 32 == 0 && BN <= BM && (EPI != GEMV_SWIGLU || WN % 64 == 0), "tile width");
+  static_assert(NCB0 <= 16 && NCB0 > 12, "group 1 issues three or four copies per wave");
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   uint8_t* lds = (uint8_t*)smem;
 
@@ -315,7 +325,7 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
   if (EPI == GEMV_SWIGLU) {  // tile columns alternate 32 gate and 32 up rows
     gB[0] = (const uint8_t*)(a.gate + (size_t)(n0 / 2) * a.K);
     gB[1] = (const uint8_t*)(a.up + (size_t)(n0 / 2) * a.K);
-  } else {  // the tile lies inside one segment (boundaries are multiples of 256)
+  } else {  // the tile lies inside one segment (boundaries are multiples of BN)
     const bf16_t* W = a.seg[0].W;
     int sb = a.seg[0].n_begin;
     for (int sg = 1; sg < a.nseg; ++sg)
@@ -357,8 +367,8 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const uint32_t ch = (uint32_t)(((4 * ks + (lane >> 4)) ^ swz) * 16);
-    fa_off[ks] = (uint32_t)(grp * WM + lr) * 128 + ch;
-    fb_off[ks] = 2 * TILE + (uint32_t)(q * WN + lr) * 128 + ch;
+    fa_off[ks] = (uint32_t)(q * WM + lr) * 128 + ch;
+    fb_off[ks] = 2 * TILE + (uint32_t)(grp * WN + lr) * 128 + ch;
   }
   bf16x8_t fa[KS][TM], fb[KS][TN];
   auto load_frags = [&](int kt) {
@@ -383,16 +393,23 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
 
   const int nk = a.K / BK;
   // k-tiles 0 and 1: waves 0-3 copy the activation tiles, 4-7 the weights
-  for (int k = 0; k < 2 && k < nk; ++k)
+  for (int k = 0; k < 2 && k < nk; ++k) {
+    if (grp == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy(k, grp == 0, q * 8 + i);
+      for (int i = 0; i < 8; ++i) copy(k, true, q * 8 + i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < (NCB + 3) / 4; ++i)
+        if (q + 4 * i < NCB) copy(k, false, q + 4 * i);
+    }
+  }
   wait_copies<0>();
   phase_barrier();
   // Phase 2kt: group 0 multiplies tile kt, group 1 reads its fragments (and
-  // copies tile kt + 2's activation rows 0-127).  Phase 2kt + 1: group 1
-  // multiplies tile kt, group 0 copies the rest of tile kt + 2 and reads tile
-  // kt + 1's fragments.  Each wave waits for its own copies of a tile before
-  // the barrier that precedes the tile's first reader.
+  // copies the weight rows of group 0's columns of tile kt + 2).  Phase
+  // 2kt + 1: group 1 multiplies tile kt, group 0 copies the rest of tile
+  // kt + 2 and reads tile kt + 1's fragments.  Each wave waits for its own
+  // copies of a tile before the barrier that precedes the tile's first reader.
   if (grp == 0) {
     load_frags(0);
     for (int kt = 0; kt < nk; ++kt) {
@@ -400,49 +417,54 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
       wait_copies<0>();
       phase_barrier();
       if (kt + 2 < nk) {
-        if (kt == 0) {  // in phase 0 group 0 was still reading tile 0's rows 0-127
+        if (kt == 0) {  // in phase 0 group 0 was still reading those rows of tile 0
 #pragma unroll
-          for (int i = 0; i < 4; ++i) copy(kt + 2, true, q * 4 + i);
+          for (int i = 0; i < 4; ++i)
+            if (q + 4 * i < NCB0) copy(kt + 2, false, q + 4 * i);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) copy(kt + 2, true, 16 + q * 4 + i);
+        for (int i = 0; i < 8; ++i) copy(kt + 2, true, q * 8 + i);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) copy(kt + 2, false, q * 8 + i);
+        for (int i = 0; i < 4; ++i)
+          if (NCB0 + q + 4 * i < NCB) copy(kt + 2, false, NCB0 + q + 4 * i);
       }
       if (kt + 1 < nk) load_frags(kt + 1);
       phase_barrier();
     }
   } else {
+    const bool four = q + 12 < NCB0;  // this wave issues four copies per k-tile, else three
     for (int kt = 0; kt < nk; ++kt) {
       const bool more = kt >= 1 && kt + 2 < nk;
       if (more) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) copy(kt + 2, true, q * 4 + i);
+        for (int i = 0; i < 4; ++i)
+          if (q + 4 * i < NCB0) copy(kt + 2, false, q + 4 * i);
       }
       load_frags(kt);
-      if (more) wait_copies<4>();  // tile kt + 1's copies done, kt + 2's may fly
-      else wait_copies<0>();
+      if (!more) wait_copies<0>();
+      else if (four) wait_copies<4>();  // tile kt + 1's copies done, kt + 2's may fly
+      else wait_copies<3>();
       phase_barrier();
       multiply();
       phase_barrier();
     }
   }
 
-  store_tile<EPI, TM, TN>(a, acc, m0 + grp * WM, n0 + q * WN, lane);
+  store_tile<EPI, TM, TN>(a, acc, m0 + q * WM, n0 + grp * WN, lane);
 }
 
-template <int EPI>
+template <int EPI, int BN>
 void launch_alt(const GemmArgs& a, int ncols, hipStream_t s) {
   const int mtiles = (a.M + 255) / 256;
-  const int nt = (ncols / 256) * mtiles;
+  const int nt = (ncols / BN) * mtiles;
   const size_t lds = (size_t)4 * 256 * 64 * 2;
   static bool attr = false;  // one-time opt-in above the default dynamic LDS limit
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)gemm_alt_kernel<EPI>,
+    (void)hipFuncSetAttribute((const void*)gemm_alt_kernel<EPI, BN>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  hipLaunchKernelGGL((gemm_alt_kernel<EPI>), dim3(nt), dim3(512), lds, s, a, mtiles);
+  hipLaunchKernelGGL((gemm_alt_kernel<EPI, BN>), dim3(nt), dim3(512), lds, s, a, mtiles);
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int BK = 64>
@@ -475,24 +497,101 @@ static int cu_count() {
   return n;
 }
 
-// ncols: tile columns (N, or 2F for SWIGLU); a multiple of 128.  Widths that
-// are multiples of 256 take 256 x 256 tiles on the alternating schedule when
-// every weight segment starts at a multiple of 256 (SwiGLU always), unless
-// 256 x 128 tiles (eight waves of 64 x 64, about 0.72 the time of a 256 x 256
-// tile) would fill the CUs in fewer rounds' worth of time.  Other widths take
-// 128 x 128 tiles.  The split of K into 64-deep tiles and 32-deep MFMA steps,
-// and so every output's bits, is the same for all of them.
+// Tile shapes for a launch.  Relative time of a round (one workgroup per
+// CU), in full rounds of 256 x 256 tiles at the same K, measured at
+// M = 2,048: 256 x 224 0.875, 256 x 128 (eight waves of 64 x 64) 0.70,
+// 128 x 128 0.45; a partial round with a fraction f of the CUs busy costs
+// (0.67 + 0.33 f) of a full one (fewer busy CUs run at a higher clock).
+enum GemmShape { SH_ALT256, SH_ALT224, SH_256X128, SH_128X128 };
+
+static double round_cost(long tiles, int cus, double per_round) {
+  const long full = tiles / cus, rest = tiles % cus;
+  return per_round * ((double)full + (rest ? 0.67 + 0.33 * (double)rest / cus : 0.0));
+}
+
+// Cheapest shape for ncols tile columns (a multiple of 128) whose weight
+// segments start at the relative columns bnd[0..nb): the alternating
+// kernels need every segment boundary on a tile boundary, 256 x 224 is not
+// used for SWIGLU (its gate/up pairs span 64 columns).
+static GemmShape best_shape(int M, int ncols, bool swiglu, const int* bnd, int nb, int cus,
+                            double* cost) {
+  auto on = [&](int w) {
+    if (ncols % w) return false;
+    for (int i = 0; i < nb; ++i)
+      if (bnd[i] % w) return false;
+    return true;
+  };
+  const long mt = (M + 255) / 256, mt2 = (M + 127) / 128;
+  GemmShape sh = SH_128X128;
+  double c = round_cost(mt2 * (ncols / 128), cus, 0.45), x;
+  if ((x = round_cost(mt * (ncols / 128), cus, 0.70)) < c) { c = x; sh = SH_256X128; }
+  if (on(256) && (x = round_cost(mt * (ncols / 256), cus, 1.0)) < c) { c = x; sh = SH_ALT256; }
+  if (!swiglu && on(224) && (x = round_cost(mt * (ncols / 224), cus, 0.875)) < c) { c = x; sh = SH_ALT224; }
+  *cost = c;
+  return sh;
+}
+
 template <int EPI>
-static void launch_epi(GemmArgs a, int ncols, bool aligned, hipStream_t s) {
-  if (ncols % 256 != 0) {
-    launch_tile<128, 128, 64, 64, EPI>(a, ncols, s);
+static void launch_shape(GemmShape sh, const GemmArgs& a, int ncols, hipStream_t s) {
+  if (sh == SH_ALT256) launch_alt<EPI, 256>(a, ncols, s);
+  else if (sh == SH_256X128) launch_tile<256, 128, 64, 64, EPI>(a, ncols, s);
+  else if (sh == SH_128X128) launch_tile<128, 128, 64, 64, EPI>(a, ncols, s);
+  else if constexpr (EPI != GEMV_SWIGLU) launch_alt<EPI, 224>(a, ncols, s);
+}
+
+// The output columns [c0, c1) of a as a launch of its own: output pointers
+// moved by c0, the segments overlapping the range clipped and rebased.
+static GemmArgs column_range(const GemmArgs& a, int c0, int c1) {
+  GemmArgs r = a;
+  r.nseg = 0;
+  for (int i = 0; i < a.nseg; ++i) {
+    const GemvSeg& g = a.seg[i];
+    const int b = std::max(g.n_begin, c0), e = std::min(g.n_end, c1);
+    if (b >= e) continue;
+    r.seg[r.nseg++] = GemvSeg{g.W + (size_t)(b - g.n_begin) * a.K, b - c0, e - c0};
+  }
+  r.out = a.out + c0;
+  if (a.out32) r.out32 = a.out32 + c0;
+  return r;
+}
+
+// ncols: tile columns (N, or 2F for SWIGLU); a multiple of 128.  The whole
+// width runs as one launch of the cheapest shape, or (STORE and RESIDUAL)
+// as two launches split at a weight segment boundary when that is cheaper:
+// the q/k/v projection of the 33B shape (9,216 columns) runs q on 256 x 224
+// tiles (256 of them at M = 2,048) and k, v on 128 x 128 tiles instead of
+// 288 tiles of 256 x 256.  The split of K into 64-deep tiles and 32-deep
+// MFMA steps, and so every output's bits, is the same for all shapes.
+template <int EPI>
+static void launch_epi(const GemmArgs& a, int ncols, hipStream_t s) {
+  const int cus = cu_count();
+  int bnd[3], nb = 0;
+  if (EPI != GEMV_SWIGLU)
+    for (int i = 0; i < a.nseg; ++i)
+      if (a.seg[i].n_begin > 0) bnd[nb++] = a.seg[i].n_begin;
+  double best;
+  GemmShape sh = best_shape(a.M, ncols, EPI == GEMV_SWIGLU, bnd, nb, cus, &best);
+  int split = 0;
+  GemmShape sl = sh, sr = sh;
+  for (int i = 0; i < nb; ++i) {
+    const int b = bnd[i];
+    if (b % 128 || b >= ncols) continue;
+    int lb[3], ln = 0, rb[3], rn = 0;
+    for (int j = 0; j < nb; ++j) {
+      if (bnd[j] < b) lb[ln++] = bnd[j];
+      else if (bnd[j] > b) rb[rn++] = bnd[j] - b;
+    }
+    double cl, cr;
+    const GemmShape l = best_shape(a.M, b, false, lb, ln, cus, &cl);
+    const GemmShape r = best_shape(a.M, ncols - b, false, rb, rn, cus, &cr);
+    if (cl + cr + 0.02 < best) { best = cl + cr + 0.02; split = b; sl = l; sr = r; }
+  }
+  if (!split) {
+    launch_shape<EPI>(sh, a, ncols, s);
     return;
   }
-  const int cus = cu_count(), mt = (a.M + 255) / 256, ct = ncols / 256;
-  const int rounds256 = (ct * mt + cus - 1) / cus;
-  const int rounds128 = (2 * ct * mt + cus - 1) / cus;
-  if (!aligned || rounds128 * 0.72 < rounds256) launch_tile<256, 128, 64, 64, EPI>(a, ncols, s);
-  else launch_alt<EPI>(a, ncols, s);
+  launch_shape<EPI>(sl, column_range(a, 0, split), split, s);
+  launch_shape<EPI>(sr, column_range(a, split, ncols), ncols - split, s);
 }
 
 void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* seg, int nseg,
@@ -511,10 +610,7 @@ void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* s
   a.ldo = ldo;
   a.out32 = out32;
   a.ld32 = ld32;
-  bool aligned = true;  // every 256-wide tile lies in one weight segment
-  if (epi != GEMV_SWIGLU)
-    for (int i = 0; i < nseg; ++i) aligned = aligned && seg[i].n_begin % 256 == 0;
-  if (epi == GEMV_STORE) launch_epi<GEMV_STORE>(a, ncols, aligned, s);
-  else if (epi == GEMV_RESIDUAL) launch_epi<GEMV_RESIDUAL>(a, ncols, aligned, s);
-  else launch_epi<GEMV_SWIGLU>(a, ncols, aligned, s);
+  if (epi == GEMV_STORE) launch_epi<GEMV_STORE>(a, ncols, s);
+  else if (epi == GEMV_RESIDUAL) launch_epi<GEMV_RESIDUAL>(a, ncols, s);
+  else launch_epi<GEMV_SWIGLU>(a, ncols, s);
 }

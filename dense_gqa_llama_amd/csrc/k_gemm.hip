@@ -271,11 +271,14 @@ void gemm_kernel(GemmArgs a, int mtiles) {
 // loads, one KiB = 8 rows of 128 bytes per copy), double-buffered: rows of
 // 64 k, chunk c of row r stored at chunk c ^ ((r >> 1) & 7), so a fragment
 // read (rows l%16, one chunk per 16 lanes) touches every bank once per 16
-// lanes.  The copies of tile kt + 2 go into tile kt's buffer as soon as both
-// groups have read it: the weight rows of group 0's columns (read by group 0
-// only) by group 1 while it reads tile kt, the rest by group 0 in the next
-// phase.  The products run in the same order as gemm_kernel's, so the two
-// give the same bits.
+// lanes.  A region of tile kt's buffer is refilled with tile kt + 2 as soon
+// as its readers are done, by the group that is loading, so the two groups
+// issue equal shares of the copies: the weight rows of group 0's columns
+// (read by group 0 only) by group 1 while it reads tile kt, the activation
+// rows (read by both) by group 0 in the next phase, and the weight rows of
+// group 1's columns (read by group 1 only) by group 1 in its next load phase.
+// The products run in the same order as gemm_kernel's, so the two give the
+// same bits.
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -290,11 +293,9 @@ __device__ __forceinline__ void phase_barrier() {
 
 template <int N>
 __device__ __forceinline__ void wait_copies() {  // at most N of this wave's copies in flight
-  static_assert(N == 0 || N == 3 || N == 4, "wait counts in use");
+  static_assert(N == 0, "wait counts in use");
   __builtin_amdgcn_sched_barrier(0);
-  if (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // NTW: weight copies carry the non-temporal hint (for projections whose
@@ -335,21 +336,22 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
     gB[0] = gB[1] = (const uint8_t*)(W + (size_t)(n0 - sb) * a.K);
   }
   const int mlast = a.M - 1 - m0;  // activation rows past M re-read the last row
+  // weight copies: a lane part (two registers) plus a uniform part taken
+  // through readfirstlane, so no per-copy offsets stay live in registers
+  const uint32_t lb0 = (uint32_t)lrow * rsB + xs0, lb1 = (uint32_t)lrow * rsB + xs1;
   auto copy = [&](int kt, bool opA, int c) {
-    const int row = 8 * c + lrow;
     const uint8_t* b;
     uint32_t go;
     if (opA) {
       b = gA;
-      go = (uint32_t)min(row, mlast) * rsA;
-    } else if (EPI == GEMV_SWIGLU) {
-      b = gB[(c >> 2) & 1];
-      go = (uint32_t)((c >> 3) * 32 + (row & 31)) * rsB;
+      go = (uint32_t)min(8 * c + lrow, mlast) * rsA + ((c & 1) ? xs1 : xs0) + (uint32_t)kt * (BK * 2);
     } else {
-      b = gB[0];
-      go = (uint32_t)row * rsB;
+      // tile row 8c + lrow; SWIGLU rows alternate 32 gate and 32 up rows
+      const uint32_t wrow = EPI == GEMV_SWIGLU ? (uint32_t)((c >> 3) * 32 + 8 * (c & 3)) : (uint32_t)(8 * c);
+      b = EPI == GEMV_SWIGLU ? gB[(c >> 2) & 1] : gB[0];
+      go = ((c & 1) ? lb1 : lb0) +
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(wrow * rsB + (uint32_t)kt * (BK * 2)));
     }
-    go += ((c & 1) ? xs1 : xs0) + (uint32_t)kt * (BK * 2);
     const int loff = (opA ? 0 : 2 * TILE) + (kt & 1) * TILE + c * 1024;
     if (NTW && !opA) __builtin_amdgcn_global_load_lds((const void*)(b + go), (lds_ptr_t)(lds + loff), 16, 0, 2);
     else __builtin_amdgcn_global_load_lds((const void*)(b + go), (lds_ptr_t)(lds + loff), 16, 0, 0);
@@ -408,11 +410,13 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
   }
   wait_copies<0>();
   phase_barrier();
-  // Phase 2kt: group 0 multiplies tile kt, group 1 reads its fragments (and
-  // copies the weight rows of group 0's columns of tile kt + 2).  Phase
-  // 2kt + 1: group 1 multiplies tile kt, group 0 copies the rest of tile
-  // kt + 2 and reads tile kt + 1's fragments.  Each wave waits for its own
-  // copies of a tile before the barrier that precedes the tile's first reader.
+  // Phase 2kt: group 0 multiplies tile kt; group 1 copies the weight rows of
+  // group 0's columns of tile kt + 2 and of its own columns of tile kt + 1,
+  // then reads tile kt's fragments.  Phase 2kt + 1: group 1 multiplies tile
+  // kt; group 0 copies tile kt + 2's activation rows and reads tile kt + 1's
+  // fragments.  A wave waits for its copies at the end of its next
+  // multiplying phase, before the barrier that precedes the copied region's
+  // first reader.
   if (grp == 0) {
     load_frags(0);
     for (int kt = 0; kt < nk; ++kt) {
@@ -427,28 +431,26 @@ __global__ __launch_bounds__(512, 1) void gemm_alt_kernel(GemmArgs a, int mtiles
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) copy(kt + 2, true, q * 8 + i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (NCB0 + q + 4 * i < NCB) copy(kt + 2, false, NCB0 + q + 4 * i);
       }
       if (kt + 1 < nk) load_frags(kt + 1);
       phase_barrier();
     }
   } else {
-    const bool four = q + 12 < NCB0;  // this wave issues four copies per k-tile, else three
     for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt >= 1 && kt + 2 < nk;
-      if (more) {
+      if (kt >= 1 && kt + 2 < nk) {  // group 0's weight rows of tile kt + 2
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (q + 4 * i < NCB0) copy(kt + 2, false, q + 4 * i);
       }
+      if (kt >= 1 && kt + 1 < nk) {  // own weight rows of tile kt + 1
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (NCB0 + q + 4 * i < NCB) copy(kt + 1, false, NCB0 + q + 4 * i);
+      }
       load_frags(kt);
-      if (!more) wait_copies<0>();
-      else if (four) wait_copies<4>();  // tile kt + 1's copies done, kt + 2's may fly
-      else wait_copies<3>();
       phase_barrier();
       multiply();
+      wait_copies<0>();
       phase_barrier();
     }
   }

@@ -128,3 +128,31 @@ def test_resumed_prompt_equals_fresh_33b_layer():
     hr = u16(model.prefill(spl, hidden=to_dev(rows[211:]), want_hidden=True)["hidden"])
     assert np.array_equal(hr, hf[211:])
     log("33B layer: split and resumed chunks equal the single chunk bit for bit")
+
+
+def test_chunk_sizes_select_other_tiles_same_bits_33b_layer():
+    """Chunks of 2,048, 1,500, 1,048 and 548 rows of one 33B-shaped layer take
+    different projection tilings (256 x 256 and 256 x 224 tiles on the
+    alternating schedule, the q/k/v projection split at the q segment's end,
+    256 x 128 and 128 x 128 tiles); every row still equals the single
+    2,048-row chunk's, and so does the cache."""
+    import synth
+    from synth.workloads import TensorIds
+    g = config(2)
+    n = 2048
+    model = gpu_model(g, n, max_chunk_rows=n, max_seqs=1)
+    rows = synth.normal_bf16(n * g.hidden, 3111, TensorIds.INPUT_ROWS).reshape(n, g.hidden)
+    fresh = model.new_sequence(n)
+    hf = u16(model.prefill(fresh, hidden=to_dev(rows), want_hidden=True)["hidden"])
+    cf = u16(fresh.view())[:, :, :n]
+    spl = model.new_sequence(n)
+    parts = []
+    for a, b in ((0, 1500), (1500, n)):
+        parts.append(u16(model.prefill(spl, hidden=to_dev(rows[a:b]), want_hidden=True)["hidden"]))
+    assert np.array_equal(np.concatenate(parts), hf)
+    assert np.array_equal(u16(spl.view())[:, :, :n], cf)
+    spl.set_length(1000)
+    hr = u16(model.prefill(spl, hidden=to_dev(rows[1000:]), want_hidden=True)["hidden"])
+    assert np.array_equal(hr, hf[1000:])
+    assert np.array_equal(u16(spl.view())[:, :, :n], cf)
+    log("33B layer: chunks of 2048 / 1500 / 548 / 1048 rows equal the single chunk bit for bit")

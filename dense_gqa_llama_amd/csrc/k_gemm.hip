@@ -46,17 +46,50 @@ struct GemmArgs {
 __device__ __forceinline__ float silu_r(float g) { return rbf(g / (1.0f + expf(-g))); }
 
 // Epilogue of a wave's TM x TN 16x16 tiles at rows r0.., tile columns c0..
-// (c0 a multiple of 64): lane l holds column l%16 and rows 4*(l/16) + r of each.
-template <int EPI, int TM, int TN>
-__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4_t (&acc)[TM][TN], int r0,
+// (c0 a multiple of 64): lane l holds column l%16 and rows 4*(l/16) + r of
+// each.  GUARD: some rows lie past M (only then are stores predicated, so a
+// whole tile's stores issue back to back).
+template <int EPI, int TM, int TN, bool GUARD>
+__device__ __forceinline__ void store_rows(const GemmArgs& a, const f32x4_t (&acc)[TM][TN], int r0,
                                            int c0, int lane) {
   const int lc = lane & 15, hrow = (lane >> 4) * 4;
+  if (EPI == GEMV_RESIDUAL) {
+    // the residual values of a batch of 16-row groups are loaded first (rows
+    // past M re-read the last row), so the wave waits for memory once per
+    // batch rather than once per row; batches of at most 112 values
+    constexpr int IB = TM * 4 * TN > 112 ? TM / 2 : TM;
+    static_assert(TM % IB == 0, "whole batches");
+#pragma unroll
+    for (int i0 = 0; i0 < TM; i0 += IB) {
+      bf16_t hv[IB][4][TN];
+#pragma unroll
+      for (int i = 0; i < IB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int mr = r0 + (i0 + i) * 16 + hrow + r;
+          const int m = GUARD ? min(mr, a.M - 1) : mr;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) hv[i][r][j] = a.out[(size_t)m * a.ldo + c0 + j * 16 + lc];
+        }
+#pragma unroll
+      for (int i = 0; i < IB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = r0 + (i0 + i) * 16 + hrow + r;
+          if (GUARD && m >= a.M) continue;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            a.out[(size_t)m * a.ldo + c0 + j * 16 + lc] = f2bf(bf2f(hv[i][r][j]) + rbf(acc[i0 + i][j][r]));
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = r0 + i * 16 + hrow + r;
-      if (m >= a.M) continue;
+      if (GUARD && m >= a.M) continue;
       if (EPI == GEMV_SWIGLU) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -70,18 +103,19 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4_t (&ac
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int n = c0 + j * 16 + lc;
-          const float v = acc[i][j][r];
-          bf16_t* o = a.out + (size_t)m * a.ldo + n;
-          if (EPI == GEMV_STORE) {
-            *o = f2bf(v);
-            if (a.out32) a.out32[(size_t)m * a.ld32 + n] = v;
-          } else {
-            *o = f2bf(bf2f(*o) + rbf(v));
-          }
+          a.out[(size_t)m * a.ldo + n] = f2bf(acc[i][j][r]);
+          if (a.out32) a.out32[(size_t)m * a.ld32 + n] = acc[i][j][r];
         }
       }
     }
   }
+}
+
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x4_t (&acc)[TM][TN], int r0,
+                                           int c0, int lane) {
+  if (r0 + TM * 16 <= a.M) store_rows<EPI, TM, TN, false>(a, acc, r0, c0, lane);
+  else store_rows<EPI, TM, TN, true>(a, acc, r0, c0, lane);
 }
 
 // Workgroup b runs on XCD b % 8; tiles are handed out so that each XCD

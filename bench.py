@@ -344,6 +344,29 @@ def main():
         normal_bf16_dev(sq.buf.data_ptr(), sq.buf.numel() // 2, 3005 + i, 0,
                         stream=stream.cuda_stream)
         sq.set_length(LONG_T)
+    # one prompt chunk of P rows at the end of the long cache (positions
+    # LONG_T + 1 - P .. LONG_T), the last of the 131k prompt's 64 chunks:
+    # whole chunk, and its attention timed on its own
+    lp0 = LONG_T + 1 - P
+    lchunk = {}
+    for rep in range(2):  # warm, then timed
+        lseqs[0].set_length(lp0)
+        if rep:
+            B.llama_set_timing(model.handle, "prefill_attn", g.n_exec)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        model.prefill(lseqs[0], tokens=prompt, want_logits=False)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            cms = a.elapsed_time(b)
+            lams, _ = B.llama_timing_read(model.handle)
+            B.llama_set_timing(model.handle, "off")
+            lchunk = {"rows": P, "pos0": lp0, "ms": round(cms, 2), "tok_s": round(P / (cms / 1e3), 1),
+                      "attention_ms": round(lams, 2),
+                      "attention_tflops": round(prefill_attn_flops(g, P, lp0) / (lams / 1e3) / 1e12, 1)}
+    lseqs[0].set_length(LONG_T)
+    log(f"long-context prompt chunk: {lchunk}")
     ltok = sd.tokens(2, gl.prompt_seeds[0], 1, g.vocab)
     model.decode(lseqs, tokens=ltok, want_logits=False, next_out=ltok)  # warm
     torch.cuda.synchronize()
@@ -365,7 +388,8 @@ def main():
                 "hbm_gbs": round(lbytes / (lms / 1e3) / 1e9, 1),
                 "attention_us_per_block": round(ams * 1e3 / max(an, 1), 2),
                 "attention_gbs": round(2 * (T_avg + 2) * kvp / g.n_exec
-                                       / (ams / max(an, 1) / 1e3) / 1e9, 1)}
+                                       / (ams / max(an, 1) / 1e3) / 1e9, 1),
+                "prompt_chunk": lchunk}
     log(f"long context: {long_ctx}")
     del lseqs
     torch.cuda.empty_cache()

@@ -3,22 +3,23 @@
 // published", section "How": prompt chunks over a position-major cache).
 //
 // One workgroup = one query head and 128 chunk rows (4 waves x 32 rows).  Key
-// tiles of 64 cache slots are staged in LDS (keys [slot][d], values
-// transposed [d][slot]), double-buffered: the next tile's global loads are in
-// flight while the current tile is consumed.  Per tile a wave computes
-// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as rows, queries as
-// columns, so each lane holds 32 scores of one query and the softmax
-// reductions stay in registers plus one xor-32 exchange), updates the running
-// max and sum in fp32 (online softmax, in base 2 with the 1/sqrt(d) scale
-// folded into the exponent), and accumulates O^T += V^T P^T.  The
-// probabilities enter that product as the sum of two bf16 parts (hi =
-// bf16(p), lo = bf16(p - hi): two MFMAs), which keeps about 16 significant
-// bits of each weight; the query rows' running state and the output
-// accumulators are fp32, and the output is rounded once to bf16.  The P^T
-// operand is the S^T accumulator registers themselves: an MFMA sums over its
-// k slots in any order, so V^T is read in the key order those registers hold.
-// The causal mask is applied only on tiles that reach past a wave's first
-// query.
+// tiles of 64 cache slots go from the cache straight into LDS (16-byte
+// LDS-direct loads, keys and values both [slot][d]), double-buffered: the
+// next tile's copies are in flight while the current tile is consumed.  Per
+// tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (keys as
+// rows, queries as columns, so each lane holds 32 scores of one query and
+// the softmax reductions stay in registers plus one xor-32 exchange), updates
+// the running max and sum in fp32 (online softmax, in base 2 with the
+// 1/sqrt(d) scale folded into the exponent), and accumulates O^T += V^T P^T.
+// The V^T operand is read with ds_read_b64_tr_b16, which transposes four
+// slots x four dims per 16 lanes on the way out of LDS.  The probabilities
+// enter that product as the sum of two bf16 parts (hi = bf16(p), lo =
+// bf16(p - hi): two MFMAs), which keeps about 16 significant bits of each
+// weight; the query rows' running state and the output accumulators are
+// fp32, and the output is rounded once to bf16.  The P^T operand is the S^T
+// accumulator registers themselves: an MFMA sums over its k slots in any
+// order, so V^T is read in the key order those registers hold.  The causal
+// mask is applied only on tiles that reach past a wave's first query.
 #include "common.h"
 #include "launch.h"
 
@@ -26,15 +27,9 @@ namespace {
 
 constexpr int QT = 128;  // chunk rows per workgroup
 constexpr int KT = 64;   // cache slots per LDS tile
-constexpr int VPAD = 8;  // V^T rows of 144 B: 16-byte fragment reads are conflict-free
 
-// Column of tile slot s in the transposed value tile.  Within each 16-slot
-// step the slots are stored in the order the PV product's k slots take them
-// (lane half h reads k slots 8h .. 8h + 7 = keys 4h .. 4h + 3, 8 + 4h .. 11 +
-// 4h): slots 0-3, 8-11, 4-7, 12-15, so a fragment is one 16-byte read.
-__device__ __forceinline__ int vcol(int s) {
-  return (s & ~15) | ((s >> 2) & 1) << 3 | ((s >> 3) & 1) << 2 | (s & 3);
-}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
@@ -53,18 +48,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
                                                            const bf16_t* __restrict__ vc,
                                                            int rows, int pos0, int nq, int nkv,
                                                            bf16_t* __restrict__ out) {
-  constexpr int KLD = D + 8;
-  constexpr int VLD = KT + VPAD;
-  constexpr int KCH = KT * D / 8 / 256;   // 16-byte key chunks per thread per tile
-  constexpr int DCH = D / 8;              // 16-byte chunks per slot
-  constexpr int VS = KT * DCH / 256;      // value slots per thread per tile
-  constexpr int NGRP = KT / VS;           // value slot groups per tile
-  static_assert(VS == 2 || VS == 4, "value staging takes 2 or 4 slots per thread");
-  static_assert(NGRP * DCH == 256 && NGRP <= 32, "value staging covers the tile");
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * KLD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][D * VLD];
-  __shared__ uint32_t sBadM[2][4][VS];  // per staging wave and slot j of a group: group bits
-  __shared__ int sBadW[2][4];           // some slot of the tile is flagged (per staging wave)
+  constexpr int CH = D / 8;             // 16-byte chunks per slot row
+  constexpr int RPI = 64 / CH;          // slot rows per LDS-direct copy (1 KiB)
+  constexpr int NPW = KT / RPI / 4;     // copies per wave per operand tile
+  static_assert(NPW * RPI * 4 == KT, "copies cover the tile");
+  // Tiles [slot][d], rows of 2D bytes, no padding.  Keys: chunk c of row r
+  // stored at c ^ (r % CH), so the 16 rows of a fragment read hit 16
+  // different chunk positions.  Values: 32-byte granule g of row r stored at
+  // g ^ (r % (CH / 2)), so the eight rows of a transposed read spread evenly.
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][KT * D];
+  __shared__ uint32_t sBad[2][4];  // per tile: slots whose value was not finite, 16 per wave
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Heaviest row blocks first over the whole grid (longest-first keeps the
@@ -100,93 +94,57 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
     for (int t = 0; t < D / 16; ++t) qf[t] = *(const bf16x8_t*)(src + 16 * t);
   }
 
-  // staging: keys as KCH chunks (slot c/DCH, dims (c%DCH)*8); values as a
-  // group of VS consecutive slots VS*(tid%NGRP) .. at dims 8*(tid/NGRP), so
-  // the 16 lanes of an LDS write fill one transposed row
-  const int vslot = VS * (tid % NGRP), vdc = 8 * (tid / NGRP);
-  u32x4_t rk[KCH], rv[VS];
-  // Slots past the block's last query are masked for every row of the block;
-  // their loads are clamped to that last slot (a valid cache row).
-  auto gload = [&](int k0) {
+  // LDS-direct copies of tile k0 into buffer buf: copy n of an operand
+  // covers tile rows n*RPI .. n*RPI + RPI - 1; lane l writes 16-byte slot l:
+  // row n*RPI + l/CH, stored chunk l%CH, so it fetches the logical chunk the
+  // swizzle puts there.  Slots past the block's last query are masked for
+  // every row of the block; their copies read that last slot (a valid row).
+  const int crow = lane / CH, cch = lane % CH;
+  auto issue = [&](int buf, int k0) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * 256, p = min(k0 + c / DCH, block_last);
-      rk[i] = *(const u32x4_t*)(kc + (size_t)p * kvd + g * D + (c % DCH) * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < VS; ++j) {
-      const int p = min(k0 + vslot + j, block_last);
-      rv[j] = *(const u32x4_t*)(vc + (size_t)p * kvd + g * D + vdc);
+    for (int m = 0; m < NPW; ++m) {
+      const int n = wave * NPW + m, r = n * RPI + crow;
+      const size_t src = (size_t)min(k0 + r, block_last) * kvd + g * D;
+      __builtin_amdgcn_global_load_lds((const void*)(kc + src + 8 * (cch ^ (r % CH))),
+                                       (lds_ptr_t)(&sK[buf][n * 512]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vc + src + 8 * (cch ^ (2 * (r % (CH / 2))))),
+                                       (lds_ptr_t)(&sV[buf][n * 512]), 16, 0, 0);
     }
   };
-  // Values are staged transposed.  On a tile where some row of the block has
-  // masked slots, a masked slot still meets a zero weight in the value
-  // product, and 0 * NaN would leak into earlier rows, so non-finite values
-  // are staged as zero there and their slot flagged: a score against a
-  // flagged slot that is not masked becomes NaN, which is what the rows
-  // attending to it get.  On the other tiles every row attends to every slot
-  // and a non-finite value reaches every row through the product itself.
+  // On a tile where some row of the block has masked slots, a masked slot
+  // still meets a zero weight in the value product, and 0 * NaN would leak
+  // into earlier rows, so there non-finite values are zeroed in LDS and their
+  // slot flagged: a score against a flagged slot that is not masked becomes
+  // NaN, which is what the rows attending to it get.  On the other tiles
+  // every row attends to every slot and a non-finite value reaches every row
+  // through the product itself.
   const int block_first = pos0 + r0;
-  auto lstore = [&](int buf, int k0) {
-    const bool masked = k0 + KT - 1 > block_first;  // uniform per workgroup
+  auto fix_values = [&](int buf) {  // four threads per slot row, CH/4 chunks each
+    constexpr int CPT = CH / 4;
+    u32x4_t* rowp = (u32x4_t*)&sV[buf][(tid >> 2) * D] + (tid & 3) * CPT;
+    uint32_t bad = 0;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + i * 256;
-      *(u32x4_t*)&sK[buf][(c / DCH) * KLD + (c % DCH) * 8] = rk[i];
-    }
-    uint32_t badj[VS];
-    uint32_t any = 0;
-#pragma unroll
-    for (int j = 0; j < VS; ++j) {
-      badj[j] = masked ? nonfinite2(rv[j].x) | nonfinite2(rv[j].y) | nonfinite2(rv[j].z) |
-                             nonfinite2(rv[j].w)
-                       : 0u;
-      any |= badj[j];
-    }
-    if (any) {  // rare: zero the non-finite halves
-#pragma unroll
-      for (int j = 0; j < VS; ++j) {
-        uint32_t w[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+    for (int c = 0; c < CPT; ++c) {
+      u32x4_t v = rowp[c];
+      const uint32_t b = nonfinite2(v.x) | nonfinite2(v.y) | nonfinite2(v.z) | nonfinite2(v.w);
+      if (b) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if ((w[e] & 0x7F80u) == 0x7F80u) w[e] &= 0xFFFF0000u;
           if ((w[e] & 0x7F800000u) == 0x7F800000u) w[e] &= 0x0000FFFFu;
         }
-        rv[j] = u32x4_t{w[0], w[1], w[2], w[3]};
+        rowp[c] = u32x4_t{w[0], w[1], w[2], w[3]};
       }
+      bad |= b;
     }
-    // transpose VS slots x eight dims into eight rows of sV
+    bad |= __shfl_xor(bad, 1, WAVE);
+    bad |= __shfl_xor(bad, 2, WAVE);
+    const uint64_t m = __ballot(bad != 0);  // bit 4k: slot 16*wave + k
+    uint32_t slots = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // dims vdc + 2e (low halves) and vdc + 2e + 1 (high halves)
-      const uint32_t w0 = rv[0][e], w1 = rv[1][e];
-      const uint32_t lo01 = (w0 & 0xFFFFu) | (w1 << 16), hi01 = (w0 >> 16) | (w1 & 0xFFFF0000u);
-      if (VS == 4) {
-        const uint32_t w2 = rv[VS > 2 ? 2 : 0][e], w3 = rv[VS > 2 ? 3 : 0][e];
-        const uint32_t lo23 = (w2 & 0xFFFFu) | (w3 << 16), hi23 = (w2 >> 16) | (w3 & 0xFFFF0000u);
-        *(uint2*)&sV[buf][(vdc + 2 * e) * VLD + vcol(vslot)] = make_uint2(lo01, lo23);
-        *(uint2*)&sV[buf][(vdc + 2 * e + 1) * VLD + vcol(vslot)] = make_uint2(hi01, hi23);
-      } else {
-        *(uint32_t*)&sV[buf][(vdc + 2 * e) * VLD + vcol(vslot)] = lo01;
-        *(uint32_t*)&sV[buf][(vdc + 2 * e + 1) * VLD + vcol(vslot)] = hi01;
-      }
-    }
-    if (!masked) {  // nothing zeroed, nothing flagged
-      if (lane == 0) sBadW[buf][wave] = 0;
-      return;
-    }
-    // per wave and slot j of a group: the groups holding a flagged value
-    // in this wave's dims (lanes l, l + NGRP, ... share a group)
-#pragma unroll
-    for (int j = 0; j < VS; ++j) {
-      uint32_t f = badj[j];
-#pragma unroll
-      for (int m = NGRP; m < WAVE; m <<= 1) f |= __shfl_xor(f, m, WAVE);
-      const uint64_t b = __ballot(f != 0);
-      if (lane == 0) sBadM[buf][wave][j] = (uint32_t)b & (uint32_t)((1ull << NGRP) - 1);
-    }
-    const int wany = __any(any != 0);
-    if (lane == 0) sBadW[buf][wave] = wany;
+    for (int k = 0; k < 16; ++k) slots |= (uint32_t)((m >> (4 * k)) & 1u) << k;
+    if (lane == 0) sBad[buf][wave] = slots;
   };
 
   f32x16_t acc[D / 32];
@@ -197,12 +155,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
   float mrow = -INFINITY, lrow = 0.f;
 
   const int ntiles = block_last / KT + 1;
-  gload(0);
-  lstore(0, 0);
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies are in LDS
   __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
     const int k0 = kt * KT, buf = kt & 1;
-    if (kt + 1 < ntiles) gload(k0 + KT);
+    if (kt + 1 < ntiles) issue(buf ^ 1, k0 + KT);
+    const bool masked = k0 + KT - 1 > block_first;  // uniform per workgroup
+    if (masked) {
+      fix_values(buf);
+      __syncthreads();
+    }
     if (k0 <= wave_last) {
       // S^T = K Q^T for 64 keys (two 32-key halves) x 32 queries
       f32x16_t s[2];
@@ -215,25 +178,25 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
       for (int t = 0; t < D / 16; ++t) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const bf16x8_t kf = *(const bf16x8_t*)&sK[buf][(32 * u + lq) * KLD + 16 * t + 8 * half];
+          const int r = 32 * u + lq;  // stored chunk of logical chunk 2t + half
+          const bf16x8_t kf = *(const bf16x8_t*)&sK[buf][r * D + 8 * ((2 * t + half) ^ (r % CH))];
           s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[u], 0, 0, 0);
         }
       }
       // keys of register r of half u: k0 + 32u + 8*(r/4) + 4*half + r%4
       // (raw scores here; the scale enters the exponent below)
       const bool diag = k0 + KT - 1 > wave_first;
-      const bool any_bad = sBadW[buf][0] | sBadW[buf][1] | sBadW[buf][2] | sBadW[buf][3];
-      if (any_bad) {  // rare: zeroed non-finite values (flag reads kept off the common path)
-        const volatile uint32_t* bm = &sBadM[buf][0][0];
-        uint32_t gm[VS];
+      if (masked && (sBad[buf][0] | sBad[buf][1] | sBad[buf][2] | sBad[buf][3])) {
+        // rare: zeroed non-finite values
+        uint32_t gm[4];
 #pragma unroll
-        for (int j = 0; j < VS; ++j) gm[j] = bm[j] | bm[VS + j] | bm[2 * VS + j] | bm[3 * VS + j];
+        for (int w = 0; w < 4; ++w) gm[w] = sBad[buf][w];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ko = 32 * u + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (gm[ko % VS] >> (ko / VS) & 1u) s[u][r] = NAN;
+            if (gm[ko >> 4] >> (ko & 15) & 1u) s[u][r] = NAN;
           }
       }
       if (diag) {  // tiles reaching past the wave's first query
@@ -284,10 +247,25 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
         }
         const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
         const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, u32x4_t{pl[0], pl[1], pl[2], pl[3]});
+        // V^T fragments: lane l needs dims 32i + l%32 of keys 16st + 8w +
+        // 4*half + e (w, e < 2, 4); a transposed read gives the 16 lanes of
+        // group gq = l/16 four slots x one dim each, lane x of the group
+        // naming slot 16st + 8w + 4*(gq/2) + x/4, dims 32i + 16*(gq%2) + 4*(x%4)..+3
         bf16x8_t vf[D / 32];
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-          vf[i] = *(const bf16x8_t*)&sV[buf][(i * 32 + lq) * VLD + 16 * st + 8 * half];
+        for (int i = 0; i < D / 32; ++i) {
+          s16x4_t p2[2];
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const int gq = lane >> 4, x = lane & 15;
+            const int row = 16 * st + 8 * w + 4 * (gq >> 1) + (x >> 2);
+            const int d = 32 * i + 16 * (gq & 1) + 4 * (x & 3);
+            const int off = row * D + 8 * ((d >> 3) ^ (2 * (row % (CH / 2)))) + (d & 7);
+            p2[w] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(&sV[buf][off]));
+          }
+          vf[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(p2[0], p2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
         // hi parts over all accumulators, then lo parts: no back-to-back
         // dependent products
 #pragma unroll
@@ -300,7 +278,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
       psum += __shfl_xor(psum, 32, WAVE);
       lrow = lrow * alpha + psum;
     }
-    if (kt + 1 < ntiles) lstore(buf ^ 1, k0 + KT);
+    // this wave's copies of the next tile are in LDS; after the barrier all
+    // are, and this tile's readers are done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 

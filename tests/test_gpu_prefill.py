@@ -121,3 +121,27 @@ def test_layer33_chunk_vs_oracle():
     fv, _ = parity.within_ulps(vcg[T:], vco[T:])
     log(f"layer33 chunk cache slots: k {fk:.5f} v {fv:.5f}")
     assert a >= 0.999 and b >= 0.999 and fk >= 0.999 and fv >= 0.999
+
+
+@pytest.mark.parametrize("cfg,n,bad", [(1, 200, 150), (2, 300, 211)])
+def test_nonfinite_row_reaches_only_later_rows(cfg, n, bad):
+    """A non-finite input row poisons its own key and value; rows before it
+    never attend to that slot (causal), so they must equal a clean run bit for
+    bit -- the masked slot's value must not leak through a zero weight
+    (0 * NaN) -- while rows from it on read NaN.  Tiny model (d = 64) and a
+    33B-shaped layer (d = 128), the bad row inside a later 64-slot tile."""
+    import synth
+    from synth.workloads import TensorIds
+    g = config(cfg)
+    model = gpu_model(g, 320, max_chunk_rows=320, max_seqs=1)
+    rows = synth.normal_bf16(n * g.hidden, 3120 + cfg, TensorIds.INPUT_ROWS).reshape(n, g.hidden)
+    clean = model.new_sequence(320)
+    hc = u16(model.prefill(clean, hidden=to_dev(rows), want_hidden=True)["hidden"])
+    poisoned = rows.copy()
+    poisoned[bad, 7] = 0x7FC0  # bf16 NaN
+    sq = model.new_sequence(320)
+    hp = u16(model.prefill(sq, hidden=to_dev(poisoned), want_hidden=True)["hidden"])
+    assert np.array_equal(hp[:bad], hc[:bad])
+    isnan = ((hp[bad:] & 0x7F80) == 0x7F80) & ((hp[bad:] & 0x007F) != 0)
+    assert isnan.any(axis=1).all()
+    log(f"config {cfg}: NaN input row {bad} of {n}: earlier rows bit-equal to the clean run, later rows NaN")

@@ -10,11 +10,11 @@
 // at 8*(l/16) of each operand, and holds output rows 4*(l/16) + j of column
 // l%16 in its four accumulators.  (The 16x16x32 form sustains a higher
 // product rate on gfx950 than 32x32x16 at the same fragment traffic per
-// product when each wave keeps the same sub-tile.)  Two kernels share that order, so every
-// output's bits are the same whichever runs and whatever M is:
-// gemm_alt_kernel (256 x 256 or 256 x 224 tiles, an alternating two-group schedule with
-// LDS-direct operand copies) and gemm_kernel (smaller tiles, register-staged
-// copies, one pinned interleaved schedule).
+// product when each wave keeps the same sub-tile.)  Two kernels share that
+// order, so every output's bits are the same whichever runs and whatever M
+// is: gemm_alt_kernel (256 x 256 or 256 x 224 tiles, an alternating
+// two-group schedule with LDS-direct operand copies) and gemm_kernel
+// (smaller tiles, register-staged copies, one pinned interleaved schedule).
 //
 // Epilogues: STORE (bf16 and optionally the fp32 sum), RESIDUAL
 // (h = bf16(h + bf16(acc))) and SWIGLU: the tile's columns alternate 32 gate

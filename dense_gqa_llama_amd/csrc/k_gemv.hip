@@ -130,6 +130,40 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   const int nv = a.K >> 3;
   const u32x4_t* xb = (const u32x4_t*)a.x;
   const int xs = a.ldx >> 3;
+  const u32x4_t* nw = (const u32x4_t*)a.normw;
+  const int cv = a.xcv;
+  const bool whole = cv >= nv;
+  constexpr int RP = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : R <= 8 ? 8 : 16;
+  // q/k: the lane that stores row r's rotated outputs reads their (cos, sin)
+  // now, so the epilogue waits on no memory.
+  float2 rc0 = {0.f, 0.f}, rc1 = {0.f, 0.f};
+  if (EPI == GEMV_QKV_ROPE && head < a.nq + a.nkv) {
+    const int r = lane >> (6 - ilog2(RP));
+    if (r < R) {
+      const size_t t = (size_t)(a.row0 + r) * (a.d >> 1) + i0;
+      rc0 = a.rope[t];
+      rc1 = a.rope[t + 1];
+    }
+  }
+  // With the norm fused and whole input rows of at most XPRE vectors per
+  // thread, the rows and the norm weight are read before the weight
+  // prefetch: they arrive first, so the rows are staged and normalised while
+  // the first weight vectors are still in flight.
+  constexpr int XPRE = 4;
+  const int tot0 = R * nv;
+  const bool pre = NORM && whole && tot0 <= XPRE * 256;
+  u32x4_t xpre[NORM ? XPRE : 1] = {}, gpre[NORM ? XPRE : 1] = {};
+  if (NORM && pre) {
+#pragma unroll
+    for (int j = 0; j < XPRE; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      if (i < tot0) {
+        const int r = i / nv, vv = i - r * nv;
+        xpre[j] = xb[r * xs + vv];
+        gpre[j] = nw[vv];
+      }
+    }
+  }
   // Software pipeline, P steps deep: the weight vectors of the next P steps
   // are in flight while this step's are consumed; the first loads are issued
   // before the input rows are staged, so the staging overlaps them.  Every
@@ -151,9 +185,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   // chunks, wave r first sums row r from memory and each chunk is normalised
   // as it is staged.  Both sums take the canonical order.
   __shared__ float srs[NORM ? R : 1];
-  const u32x4_t* nw = (const u32x4_t*)a.normw;
-  const int cv = a.xcv;
-  const bool whole = cv >= nv;
+  if (NORM && pre) {
+#pragma unroll
+    for (int j = 0; j < XPRE; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      if (i < tot0) sx[i] = xpre[j];
+    }
+    __syncthreads();
+    if (wave < R) {
+      const float rs = row_inv_rms_lds(sx + wave * cv, a.K, a.eps);
+      if (lane == 0) srs[wave] = rs;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < XPRE; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      if (i < tot0) sx[i] = norm8(xpre[j], gpre[j], srs[i / nv]);
+    }
+    __syncthreads();
+  }
   if (NORM && !whole) {
     if (wave < R) {
       const float rs = row_inv_rms(a.x + (size_t)wave * a.ldx, a.K, a.eps);
@@ -163,7 +213,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
   int c0 = 0;
   for (int base = 0; base < nv; base += P * WAVE) {
-    if (base % cv == 0) {
+    if (base % cv == 0 && !(NORM && pre)) {
       if (base) __syncthreads();  // the previous chunk's readers are done
       const int cn = min(cv, nv - base), tot = R * cn;
       // XU vectors per thread and pass; past the end a thread repeats the
@@ -233,7 +283,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
   // Lane sums, scattered so that one lane holds each output's sums (rows
   // padded to a power of two with zeros), then one store per lane.
-  constexpr int RP = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : R <= 8 ? 8 : 16;
   if (EPI == GEMV_QKV_ROPE) {
     // one group per row: its four outputs (two rotation pairs) in one lane
     float v[RP][4];
@@ -261,7 +310,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       } else {
         dst = head < a.nq ? a.out + (size_t)rt * a.ldo + head * a.d + i0
                           : a.tab.k[seq] + (size_t)p * kvd + (head - a.nq) * a.d + i0;
-        const float2 c0 = a.rope[(size_t)rt * half + i0], c1 = a.rope[(size_t)rt * half + i0 + 1];
+        const float2 c0 = rc0, c1 = rc1;
         dst[0] = f2bf(rbf(x0 * c0.x) + rbf(-y0 * c0.y));
         dst[half] = f2bf(rbf(y0 * c0.x) + rbf(x0 * c0.y));
         dst[1] = f2bf(rbf(x1 * c1.x) + rbf(-y1 * c1.y));

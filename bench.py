@@ -166,7 +166,7 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path "
+        print("bench.py runs on one GPU: the forward step has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 

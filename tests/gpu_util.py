@@ -17,14 +17,17 @@ _PROGRESS = []
 
 
 def log(msg):
-    """Prints a progress line and appends it to gpurun_out/gpu_tests_progress.log
-    (pytest holds a test's own output until it ends; the file shows a long test
+    """Prints a progress line and, when the environment names a directory in
+    GPU_TESTS_PROGRESS_DIR, appends it to gpu_tests_progress.log there (pytest
+    holds a test's own output until it ends; the file shows a long test
     advancing while it runs)."""
     print(msg, flush=True)
     sys.stdout.flush()
+    d = os.environ.get("GPU_TESTS_PROGRESS_DIR")
+    if not d:
+        return
     try:
         if not _PROGRESS:
-            d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
             os.makedirs(d, exist_ok=True)
             _PROGRESS.append(open(os.path.join(d, "gpu_tests_progress.log"), "a"))
         _PROGRESS[0].write(msg + "\n")

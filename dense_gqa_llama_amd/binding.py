@@ -40,7 +40,7 @@ class llama_config(ctypes.Structure):
                 ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_float),
                 ("max_chunk_rows", ctypes.c_int32), ("max_window_rows", ctypes.c_int32),
-                ("max_seqs", ctypes.c_int32)]
+                ("max_seqs", ctypes.c_int32), ("prompt_exact", ctypes.c_int32)]
 
 
 BLOCK_FIELDS = ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down")
@@ -61,13 +61,19 @@ _SIGS = {
     "llama_kv_alloc": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_size_t,
                                       ctypes.POINTER(_P)]),
     "llama_kv_length": (ctypes.c_int32, [_P]),
-    "llama_kv_set_length": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "llama_kv_truncate": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "llama_test_kv_declare": (ctypes.c_int, [_P, ctypes.c_int32]),
     "llama_kv_slab": (_P, [_P, ctypes.c_int32, ctypes.c_int32]),
     "llama_prefill_chunk": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                            _P, ctypes.c_int32, _P, _P]),
     "llama_decode_step": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.c_int32, _P, _P,
                                          ctypes.c_int32, _P, _P, _P, _P, _P]),
     "llama_set_capture": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
+    "llama_set_probe": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_int32]),
+    "llama_test_linear": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                         ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "llama_test_attention": (ctypes.c_int, [_P, ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                            ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "llama_check_finite": (ctypes.c_int, [_P, _P]),
     "llama_sample": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                     ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
@@ -125,10 +131,11 @@ def _check(rc):
 
 
 def make_config(n_blocks, n_loops, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab,
-                rope_theta, rms_eps, max_chunk_rows=2048, max_window_rows=16, max_seqs=2):
+                rope_theta, rms_eps, max_chunk_rows=2048, max_window_rows=16, max_seqs=2,
+                prompt_exact=0):
     return llama_config(n_blocks, n_loops, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab,
                         float(rope_theta), float(rms_eps), max_chunk_rows, max_window_rows,
-                        max_seqs)
+                        max_seqs, int(prompt_exact))
 
 
 def llama_workspace_bytes(cfg, max_positions):
@@ -163,8 +170,12 @@ def llama_kv_length(kv):
     return lib.llama_kv_length(kv)
 
 
-def llama_kv_set_length(kv, n):
-    return _check(lib.llama_kv_set_length(kv, n))
+def llama_kv_truncate(kv, n):
+    return _check(lib.llama_kv_truncate(kv, n))
+
+
+def llama_test_kv_declare(kv, n):
+    return _check(lib.llama_test_kv_declare(kv, n))
 
 
 def llama_kv_slab(kv, exec_index, which):
@@ -187,6 +198,34 @@ def llama_decode_step(model, kvs, tokens, hidden_in, rows, hidden_out=None, logi
 
 def llama_set_capture(model, buf, nbytes):
     return _check(lib.llama_set_capture(model, buf, nbytes))
+
+
+PROBE_FIELDS = ("h_in", "x_attn", "qkv32", "q_rope", "attn", "attn32", "o32", "x_mlp",
+                "gate_up32", "act", "down32")
+
+
+class llama_probe(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in PROBE_FIELDS]
+
+
+def llama_set_probe(model, exec_index, buffers, max_rows):
+    """buffers: dict field -> device address (missing fields are NULL), or
+    None to clear the hook."""
+    if buffers is None:
+        return _check(lib.llama_set_probe(model, 0, None, 0))
+    pr = llama_probe(*[buffers.get(f) for f in PROBE_FIELDS])
+    return _check(lib.llama_set_probe(model, exec_index, ctypes.byref(pr), max_rows))
+
+
+def llama_test_linear(model, prompt_kernel, x, rows, w, n, k, y, y32, stream=None):
+    return _check(lib.llama_test_linear(model, int(prompt_kernel), x, rows, w, n, k, y, y32,
+                                        stream))
+
+
+def llama_test_attention(model, prompt_kernel, kv, exec_index, q, rows, pos0, out, out32=None,
+                         stream=None):
+    return _check(lib.llama_test_attention(model, int(prompt_kernel), kv, exec_index, q, rows,
+                                           pos0, out, out32, stream))
 
 
 def llama_check_finite(model, stream=None):

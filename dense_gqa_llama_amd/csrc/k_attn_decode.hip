@@ -133,14 +133,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
     lt += __shfl_xor(lt, 32, WAVE);
     lrun = lrun * alpha + lt;
     mrun = mnew;
-    // o = o * alpha + sum over the tile's slots of e v (weights from lane
-    // h + 16(u/4), register u%4, for slot u)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
-      o0[h] *= a;
-      o1[h] *= a;
-    }
+    // o = o * alpha + (sum over the tile's slots of e v), the tile's sum
+    // formed on its own first (weights from lane h + 16(u/4), register u%4,
+    // for slot u): each running sum takes one rounding per tile, so its error
+    // does not grow with the number of slots a wave walks.
+    float t0[G], t1[G];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const float v0 = bf_lo(vv[j]), v1 = bf_hi(vv[j]);
@@ -155,9 +152,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
           const float w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e[u1 % 4]), h + 16 * (u1 / 4)));
           w = vg ? w1 : w0;
         }
-        o0[h] = fmaf(w, v0, o0[h]);
-        o1[h] = fmaf(w, v1, o1[h]);
+        t0[h] = j ? fmaf(w, v0, t0[h]) : w * v0;
+        t1[h] = j ? fmaf(w, v1, t1[h]) : w * v1;
       }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+      o0[h] = fmaf(o0[h], a, t0[h]);
+      o1[h] = fmaf(o1[h], a, t1[h]);
     }
   };
   if (ntile > 0) {
@@ -211,7 +214,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
 template <int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__ part,
                                                        RowTable tab, int nq,
-                                                       bf16_t* __restrict__ out) {
+                                                       bf16_t* __restrict__ out,
+                                                       float* __restrict__ out32) {
   __shared__ float wts[MAXB];
   __shared__ float lsum[MAXB];
   const int h = blockIdx.x, rt = blockIdx.y, j = threadIdx.x;
@@ -243,23 +247,24 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
     }
   }
   out[((size_t)rt * nq + h) * D + j] = f2bf(O / L);
+  if (out32) out32[((size_t)rt * nq + h) * D + j] = O / L;  // parity probe
 }
 
 template <int D, int G>
 void launch_dg(const void* q, const RowTable& tab, int rows, int nq, int nkv, float* part,
-               int nb_launch, void* out, hipStream_t s) {
+               int nb_launch, void* out, float* out32, hipStream_t s) {
   hipLaunchKernelGGL((attn_decode_kernel<D, G>), dim3(nb_launch, nkv, rows), dim3(256), 0, s,
                      (const bf16_t*)q, tab, nq, nkv, part);
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(nq, rows), dim3(D), 0, s, part, tab, nq,
-                     (bf16_t*)out);
+                     (bf16_t*)out, out32);
 }
 
 template <int D>
 void launch_d(int G, const void* q, const RowTable& tab, int rows, int nq, int nkv, float* part,
-              int nb_launch, void* out, hipStream_t s) {
+              int nb_launch, void* out, float* out32, hipStream_t s) {
   switch (G) {
 #define CASE(g) \
-  case g: launch_dg<D, g>(q, tab, rows, nq, nkv, part, nb_launch, out, s); break;
+  case g: launch_dg<D, g>(q, tab, rows, nq, nkv, part, nb_launch, out, out32, s); break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
 #undef CASE
     default: break;
@@ -279,7 +284,7 @@ int attn_max_blocks() { return MAXB; }
 // q: [rows][nq][d] after RoPE; out: [rows][nq][d].  part holds
 // rows * nq * 64 * (d + 2) floats.
 void launch_attn_decode(const void* q, const RowTable& tab, int rows, int nq, int nkv, int d,
-                        float* part, void* out, hipStream_t s) {
+                        float* part, void* out, float* out32, hipStream_t s) {
   int nb_launch = 1;
   int nseq = (rows + tab.rows_per_seq - 1) / tab.rows_per_seq;
   for (int i = 0; i < nseq; ++i)
@@ -288,6 +293,6 @@ void launch_attn_decode(const void* q, const RowTable& tab, int rows, int nq, in
       nb_launch = max(nb_launch, p / host_block_slots(p) + 1);
     }
   int G = nq / nkv;
-  if (d == 64) launch_d<64>(G, q, tab, rows, nq, nkv, part, nb_launch, out, s);
-  else launch_d<128>(G, q, tab, rows, nq, nkv, part, nb_launch, out, s);
+  if (d == 64) launch_d<64>(G, q, tab, rows, nq, nkv, part, nb_launch, out, out32, s);
+  else launch_d<128>(G, q, tab, rows, nq, nkv, part, nb_launch, out, out32, s);
 }

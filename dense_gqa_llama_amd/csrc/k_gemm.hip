@@ -16,6 +16,13 @@
 // two-group schedule with LDS-direct operand copies) and gemm_kernel
 // (smaller tiles, register-staged copies, one pinned interleaved schedule).
 //
+// Exact form: the matrix unit's own accumulation loses more than one fp32
+// addition per product (a chain of 224 products at K = 7,168 carries a
+// signed error of ~7.5 fp32 steps at the row's RMS, binary64 as reference,
+// where the decode projections' lane sums carry ~1.3), so on request the
+// running sums restart every 128 terms into fp32 totals: ~2.1 steps, at about
+// twice the time (256 x 128 tiles of the register-staged kernel).
+//
 // Epilogues: STORE (bf16 and optionally the fp32 sum), RESIDUAL
 // (h = bf16(h + bf16(acc))) and SWIGLU: the tile's columns alternate 32 gate
 // rows and the same 32 up rows of the weights, so one wave holds g and u of
@@ -131,7 +138,7 @@ __device__ __forceinline__ int xcd_tile(int b, int nt) {
 // (rows padded to BK + 8 elements); each wave owns a WM x WN sub-tile of
 // 16x16 MFMA tiles.  Register budget: two waves per SIMD (two workgroups per
 // CU when a workgroup has four waves).
-template <int BM, int BN, int WM, int WN, int EPI, int BK>
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int FLUSH = 0>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, (BM / WM) * (BN / WN) <= 4 ? 2 : 1)
 void gemm_kernel(GemmArgs a, int mtiles) {
   constexpr int LDK = BK + 8;   // LDS row stride (bf16): 16-byte fragment reads stay conflict-free
@@ -274,6 +281,29 @@ void gemm_kernel(GemmArgs a, int mtiles) {
     __syncthreads();
   };
 
+  // FLUSH > 0: every FLUSH k-tiles the matrix unit's running sums are added
+  // to fp32 totals and restarted from zero, so each chain of products
+  // accumulates only FLUSH * BK terms (the matrix unit's internal additions
+  // lose more than an fp32 addition per product; short chains keep their
+  // error at the scale of a partial sum).
+  f32x4_t mst[FLUSH ? TM : 1][FLUSH ? TN : 1];
+  auto flush = [&](int kt) {
+    if constexpr (FLUSH > 0) {
+      if ((kt + 1) % FLUSH == 0 || kt + 1 == nk) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              mst[i][j][r] = kt + 1 == FLUSH || (kt + 1 < FLUSH && kt + 1 == nk)
+                                 ? acc[i][j][r] : mst[i][j][r] + acc[i][j][r];
+              acc[i][j][r] = 0.f;
+            }
+          }
+      }
+    }
+  };
   gload(0, 0);
   gload(1, 1);
   lstore(0, 0);
@@ -281,11 +311,17 @@ void gemm_kernel(GemmArgs a, int mtiles) {
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     step(kt, 0);
+    flush(kt);
     step(kt + 1, 1);
+    flush(kt + 1);
   }
-  if (kt < nk) step(kt, 0);
+  if (kt < nk) {
+    step(kt, 0);
+    flush(kt);
+  }
 
-  store_tile<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, lane);
+  if constexpr (FLUSH > 0) store_tile<EPI, TM, TN>(a, mst, m0 + wm * WM, n0 + wn * WN, lane);
+  else store_tile<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -516,18 +552,18 @@ void launch_alt(const GemmArgs& a, int ncols, hipStream_t s) {
   else launch_alt_nt<EPI, BN, false>(a, ncols, s);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int BK = 64>
+template <int BM, int BN, int WM, int WN, int EPI, int BK = 64, int FLUSH = 0>
 void launch_tile(const GemmArgs& a, int ncols, hipStream_t s) {
   const int mtiles = (a.M + BM - 1) / BM;
   const int nt = (ncols / BN) * mtiles;
   const size_t lds = (size_t)2 * (BM + BN) * (BK + 8) * sizeof(bf16_t);
   static bool attr = false;  // one-time opt-in above the default dynamic LDS limit
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)gemm_kernel<BM, BN, WM, WN, EPI, BK>,
+    (void)hipFuncSetAttribute((const void*)gemm_kernel<BM, BN, WM, WN, EPI, BK, FLUSH>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, BK>), dim3(nt),
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, BK, FLUSH>), dim3(nt),
                      dim3((BM / WM) * (BN / WN) * 64), lds, s, a, mtiles);
 }
 
@@ -643,9 +679,17 @@ static void launch_epi(const GemmArgs& a, int ncols, hipStream_t s) {
   launch_shape<EPI>(sr, column_range(a, split, ncols), ncols - split, s);
 }
 
+// Exact form: 256 x 128 tiles of the register-staged kernel whose running
+// sums restart every two k-tiles (128 terms) into fp32 totals; every output
+// still sums its k-tiles in increasing order.
+template <int EPI>
+static void launch_exact(const GemmArgs& a, int ncols, hipStream_t s) {
+  launch_tile<256, 128, 64, 64, EPI, 64, 2>(a, ncols, s);
+}
+
 void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* seg, int nseg,
                  const void* gate, const void* up, void* out, int ldo, float* out32, int ld32,
-                 int ncols, hipStream_t s) {
+                 int ncols, bool exact, hipStream_t s) {
   GemmArgs a{};
   a.A = (const bf16_t*)A;
   a.lda = lda;
@@ -659,6 +703,12 @@ void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* s
   a.ldo = ldo;
   a.out32 = out32;
   a.ld32 = ld32;
+  if (exact) {
+    if (epi == GEMV_STORE) launch_exact<GEMV_STORE>(a, ncols, s);
+    else if (epi == GEMV_RESIDUAL) launch_exact<GEMV_RESIDUAL>(a, ncols, s);
+    else launch_exact<GEMV_SWIGLU>(a, ncols, s);
+    return;
+  }
   if (epi == GEMV_STORE) launch_epi<GEMV_STORE>(a, ncols, s);
   else if (epi == GEMV_RESIDUAL) launch_epi<GEMV_RESIDUAL>(a, ncols, s);
   else launch_epi<GEMV_SWIGLU>(a, ncols, s);

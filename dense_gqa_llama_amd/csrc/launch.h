@@ -68,16 +68,19 @@ void launch_gemv_qkv_rope(const GemvSeg* seg, int K, const void* x, int ldx, int
 
 // Prompt-chunk projections on the matrix cores; ncols tile columns (N, or
 // 2F for SWIGLU, whose tiles interleave 32 gate and 32 up rows).
+// exact: the projections' running sums restart every 128 terms (slower).
 void launch_gemm(int epi, const void* A, int lda, int M, int K, const GemvSeg* seg, int nseg,
                  const void* gate, const void* up, void* out, int ldo, float* out32, int ld32,
-                 int ncols, hipStream_t s);
+                 int ncols, bool exact, hipStream_t s);
 // Prompt-chunk attention: rows at positions [pos0, pos0 + rows) against the
-// cache slabs kc / vc of one sequence.
+// cache slabs kc / vc of one sequence; out32 (nullable) also receives the
+// output before its rounding.
+// exact: three-part weights, per-tile sums (slower).
 void launch_attn_prefill(const void* q, const void* kc, const void* vc, int rows, int pos0, int nq,
-                         int nkv, int d, void* out, hipStream_t s);
+                         int nkv, int d, void* out, float* out32, bool exact, hipStream_t s);
 
 // Decode attention: split over key blocks at absolute positions, then
-// merged in block order.
+// merged in block order; out32 (nullable) as for prompt chunks.
 int attn_max_blocks();
 void launch_attn_decode(const void* q, const RowTable& tab, int rows, int nq, int nkv, int d,
-                        float* part, void* out, hipStream_t s);
+                        float* part, void* out, float* out32, hipStream_t s);

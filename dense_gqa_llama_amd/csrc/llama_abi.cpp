@@ -118,6 +118,8 @@ int check_config(const llama_config* c) {
     return fail(LLAMA_E_GEOMETRY, "max_window_rows must be 1..16");
   if (c->max_seqs < 1 || c->max_seqs > LLAMA_MAX_SEQS)
     return fail(LLAMA_E_GEOMETRY, "max_seqs must be 1..%d", LLAMA_MAX_SEQS);
+  if (c->prompt_exact != 0 && c->prompt_exact != 1)
+    return fail(LLAMA_E_ARG, "prompt_exact must be 0 or 1");
   return LLAMA_OK;
 }
 
@@ -135,6 +137,10 @@ struct llama_model {
   int max_positions;
   void* cap;
   size_t cap_bytes;
+  // parity probe of one execution (test hook)
+  int probe_exec = -1;
+  int probe_rows = 0;
+  llama_probe probe{};
   bool flag_ready;  // the non-finite flag has been cleared on the device
   // measurement hook
   int timing_kernel = 0;
@@ -222,7 +228,10 @@ bool norm_fused(bool chunk, int rows) { return !chunk && rows <= GEMV_NORM_ROWS;
 // Runs the block stack over the pass's rows.  On return ws.h holds the
 // residual after the last execution and, when the model has a vocabulary and
 // the norm is not fused, ws.x the final-normed rows.  cap_row0 / cap_rows
-// place these rows in the capture buffer.
+// place these rows in the capture buffer.  While the parity probe is set,
+// its execution also writes the probe's intermediate values (extra launches
+// of the same kernels with storing epilogues, into the caller's buffers;
+// their bf16 outputs land in workspace regions that are dead at that point).
 void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, int cap_row0,
                int cap_rows, bool chunk) {
   llama_model* m = p.m;
@@ -239,6 +248,8 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
   void* rope = m->ws + m->L.rope;
   const size_t rowb = (size_t)d.H * 2;
   const bool fuse = norm_fused(chunk, rows);
+  const bool ex = c.prompt_exact != 0;
+  const int nqkv = d.qd + 2 * d.kvd;
 
   if (tok) launch_embed(m->embed, d.V, d.H, tok, h, rows, p.s);
   else (void)hipMemcpyAsync(h, hin, rows * rowb, hipMemcpyDeviceToDevice, p.s);
@@ -249,42 +260,70 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
       const int e = loop * c.n_blocks + b;
       const llama_block_weights& w = m->blocks[b];
       RowTable tab = table_for(p, e);
+      const bool pr = m->probe_exec == e;
+      const llama_probe& P = m->probe;
+      auto pcopy = [&](void* dst, const void* src, size_t width_bytes) {
+        if (pr && dst)
+          (void)hipMemcpyAsync(dst, src, rows * width_bytes, hipMemcpyDeviceToDevice, p.s);
+      };
+      // the normed input of a projection, into the probe: copied when the
+      // step normalises into ws.x, else by the same norm kernel
+      auto pnorm = [&](void* dst, const void* normw) {
+        if (!pr || !dst) return;
+        if (fuse) launch_rmsnorm(h, normw, dst, rows, d.H, c.rms_eps, p.s);
+        else pcopy(dst, x, rowb);
+      };
+      pcopy(P.h_in, h, rowb);
 
       if (!fuse) launch_rmsnorm(h, w.attn_norm, x, rows, d.H, c.rms_eps, p.s);
+      pnorm(P.x_attn, w.attn_norm);
       GemvSeg qkvseg[3] = {{(const uint16_t*)w.q, 0, d.qd},
                            {(const uint16_t*)w.k, d.qd, d.qd + d.kvd},
                            {(const uint16_t*)w.v, d.qd + d.kvd, d.qd + 2 * d.kvd}};
-      const int nqkv = d.qd + 2 * d.kvd;
       GemvSeg oseg[1] = {{(const uint16_t*)w.o, 0, d.H}};
       if (chunk) {
         {
           Timed t(m, LLAMA_TIMING_PREFILL_GEMM, p.s);
           launch_gemm(GEMV_STORE, x, d.H, rows, d.H, qkvseg, 3, nullptr, nullptr, qkv, nqkv,
-                      nullptr, 0, nqkv, p.s);
+                      pr ? P.qkv32 : nullptr, nqkv, nqkv, ex, p.s);
         }
         launch_rope_kv(qkv, q, tab, rows, d.nq, d.nkv, d.d, rope, p.s);
+        pcopy(P.q_rope, q, (size_t)d.qd * 2);
         {
           Timed t(m, LLAMA_TIMING_PREFILL_ATTN, p.s);
-          launch_attn_prefill(q, tab.k[0], tab.v[0], rows, p.pos0[0], d.nq, d.nkv, d.d, att, p.s);
+          launch_attn_prefill(q, tab.k[0], tab.v[0], rows, p.pos0[0], d.nq, d.nkv, d.d, att,
+                              pr ? P.attn32 : nullptr, ex, p.s);
         }
+        pcopy(P.attn, att, (size_t)d.qd * 2);
+        if (pr && P.o32)
+          launch_gemm(GEMV_STORE, att, d.qd, rows, d.qd, oseg, 1, nullptr, nullptr, x, d.H, P.o32,
+                      d.H, d.H, ex, p.s);
         {
           Timed t(m, LLAMA_TIMING_PREFILL_GEMM, p.s);
           launch_gemm(GEMV_RESIDUAL, att, d.qd, rows, d.qd, oseg, 1, nullptr, nullptr, h, d.H,
-                      nullptr, 0, d.H, p.s);
+                      nullptr, 0, d.H, ex, p.s);
         }
       } else {
+        const uint16_t* in = fuse ? h : x;
+        if (pr && P.qkv32)  // same sums as the fused launch; bf16 results unused
+          gemv_rows(GEMV_STORE, qkvseg, 3, nqkv, d.H, in, d.H, rows, qkv, nqkv, P.qkv32, nqkv,
+                    p.s, fuse ? w.attn_norm : nullptr, c.rms_eps);
         {
           Timed t(m, LLAMA_TIMING_QKV, p.s);
-          const uint16_t* in = fuse ? h : x;
           for (int r0 = 0; r0 < rows; r0 += 16)
             launch_gemv_qkv_rope(qkvseg, d.H, in + (size_t)r0 * d.H, d.H, std::min(16, rows - r0),
                                  r0, q, tab, rope, d.nq, d.nkv, d.d, fuse ? w.attn_norm : nullptr,
                                  c.rms_eps, p.s);
         }
+        pcopy(P.q_rope, q, (size_t)d.qd * 2);
         {
           Timed t(m, LLAMA_TIMING_ATTN, p.s);
-          launch_attn_decode(q, tab, rows, d.nq, d.nkv, d.d, part, att, p.s);
+          launch_attn_decode(q, tab, rows, d.nq, d.nkv, d.d, part, att, pr ? P.attn32 : nullptr,
+                             p.s);
         }
+        pcopy(P.attn, att, (size_t)d.qd * 2);
+        if (pr && P.o32)
+          gemv_rows(GEMV_STORE, oseg, 1, d.H, d.qd, att, d.qd, rows, x, d.H, P.o32, d.H, p.s);
         {
           Timed t(m, LLAMA_TIMING_O, p.s);
           gemv_rows(GEMV_RESIDUAL, oseg, 1, d.H, d.qd, att, d.qd, rows, h, d.H, nullptr, 0, p.s);
@@ -295,25 +334,50 @@ void run_stack(const Pass& p, const int32_t* tok, const void* hin, void* hout, i
                          rowb, h, rowb, rowb, rows, hipMemcpyDeviceToDevice, p.s);
 
       if (!fuse) launch_rmsnorm(h, w.mlp_norm, x, rows, d.H, c.rms_eps, p.s);
-      GemvSeg gu[2] = {{(const uint16_t*)w.gate, 0, d.F}, {(const uint16_t*)w.up, 0, d.F}};
+      pnorm(P.x_mlp, w.mlp_norm);
+      GemvSeg gseg[1] = {{(const uint16_t*)w.gate, 0, d.F}};
+      GemvSeg useg[1] = {{(const uint16_t*)w.up, 0, d.F}};
+      GemvSeg gu[2] = {gseg[0], useg[0]};
       GemvSeg dseg[1] = {{(const uint16_t*)w.down, 0, d.H}};
+      const bool pgu = pr && P.gate_up32;
       if (chunk) {
-        Timed t(m, LLAMA_TIMING_PREFILL_GEMM, p.s);
-        launch_gemm(GEMV_SWIGLU, x, d.H, rows, d.H, nullptr, 0, w.gate, w.up, mm, d.F, nullptr, 0,
-                    2 * d.F, p.s);
-        launch_gemm(GEMV_RESIDUAL, mm, d.F, rows, d.F, dseg, 1, nullptr, nullptr, h, d.H, nullptr,
-                    0, d.H, p.s);
+        if (pgu) {  // bf16 results land in ws.m before the SwiGLU launch rewrites it
+          launch_gemm(GEMV_STORE, x, d.H, rows, d.H, gseg, 1, nullptr, nullptr, mm, d.F,
+                      P.gate_up32, 2 * d.F, d.F, ex, p.s);
+          launch_gemm(GEMV_STORE, x, d.H, rows, d.H, useg, 1, nullptr, nullptr, mm, d.F,
+                      P.gate_up32 + d.F, 2 * d.F, d.F, ex, p.s);
+        }
+        {
+          Timed t(m, LLAMA_TIMING_PREFILL_GEMM, p.s);
+          launch_gemm(GEMV_SWIGLU, x, d.H, rows, d.H, nullptr, 0, w.gate, w.up, mm, d.F, nullptr,
+                      0, 2 * d.F, ex, p.s);
+          launch_gemm(GEMV_RESIDUAL, mm, d.F, rows, d.F, dseg, 1, nullptr, nullptr, h, d.H,
+                      nullptr, 0, d.H, ex, p.s);
+        }
+        if (pr && P.down32)
+          launch_gemm(GEMV_STORE, mm, d.F, rows, d.F, dseg, 1, nullptr, nullptr, x, d.H, P.down32,
+                      d.H, d.H, ex, p.s);
       } else {
+        const uint16_t* in = fuse ? h : x;
+        if (pgu) {
+          gemv_rows(GEMV_STORE, gseg, 1, d.F, d.H, in, d.H, rows, mm, d.F, P.gate_up32, 2 * d.F,
+                    p.s, fuse ? w.mlp_norm : nullptr, c.rms_eps);
+          gemv_rows(GEMV_STORE, useg, 1, d.F, d.H, in, d.H, rows, mm, d.F, P.gate_up32 + d.F,
+                    2 * d.F, p.s, fuse ? w.mlp_norm : nullptr, c.rms_eps);
+        }
         {
           Timed t(m, LLAMA_TIMING_GATE_UP, p.s);
-          gemv_rows(GEMV_SWIGLU, gu, 2, d.F, d.H, fuse ? h : x, d.H, rows, mm, d.F, nullptr, 0,
-                    p.s, fuse ? w.mlp_norm : nullptr, c.rms_eps);
+          gemv_rows(GEMV_SWIGLU, gu, 2, d.F, d.H, in, d.H, rows, mm, d.F, nullptr, 0, p.s,
+                    fuse ? w.mlp_norm : nullptr, c.rms_eps);
         }
         {
           Timed t(m, LLAMA_TIMING_DOWN, p.s);
           gemv_rows(GEMV_RESIDUAL, dseg, 1, d.H, d.F, mm, d.F, rows, h, d.H, nullptr, 0, p.s);
         }
+        if (pr && P.down32)
+          gemv_rows(GEMV_STORE, dseg, 1, d.H, d.F, mm, d.F, rows, x, d.H, P.down32, d.H, p.s);
       }
+      pcopy(P.act, mm, (size_t)d.F * 2);
       if (m->cap)
         (void)hipMemcpy2DAsync((uint8_t*)m->cap + (((size_t)e * 2 + 1) * cap_rows + cap_row0) * rowb,
                          rowb, h, rowb, rowb, rows, hipMemcpyDeviceToDevice, p.s);
@@ -459,7 +523,15 @@ int llama_kv_alloc(llama_model* m, int32_t max_positions, void* device_buf, size
 
 int32_t llama_kv_length(const llama_kv* kv) { return kv ? kv->length : -1; }
 
-int llama_kv_set_length(llama_kv* kv, int32_t n) {
+int llama_kv_truncate(llama_kv* kv, int32_t n) {
+  if (!kv) return fail(LLAMA_E_ARG, "cache handle is NULL");
+  if (n < 0 || n > kv->length)
+    return fail(LLAMA_E_POSITION, "cannot keep %d positions of a cache holding %d", n, kv->length);
+  kv->length = n;
+  return LLAMA_OK;
+}
+
+int llama_test_kv_declare(llama_kv* kv, int32_t n) {
   if (!kv) return fail(LLAMA_E_ARG, "cache handle is NULL");
   if (n < 0 || n > kv->max_positions)
     return fail(LLAMA_E_CAPACITY, "length %d outside 0..%d", n, kv->max_positions);
@@ -479,7 +551,27 @@ int llama_set_capture(llama_model* m, void* buf, size_t bytes) {
   return LLAMA_OK;
 }
 
+int llama_set_probe(llama_model* m, int32_t exec, const llama_probe* probe, int32_t max_rows) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  if (!probe) {
+    m->probe_exec = -1;
+    m->probe_rows = 0;
+    m->probe = llama_probe{};
+    return LLAMA_OK;
+  }
+  if (exec < 0 || exec >= m->d.nexec)
+    return fail(LLAMA_E_ARG, "execution %d outside 0..%d", exec, m->d.nexec - 1);
+  if (max_rows < 1) return fail(LLAMA_E_ARG, "max_rows must be positive");
+  m->probe_exec = exec;
+  m->probe_rows = max_rows;
+  m->probe = *probe;
+  return LLAMA_OK;
+}
+
 static int check_capture(llama_model* m, int rows) {
+  if (m->probe_exec >= 0 && rows > m->probe_rows)
+    return fail(LLAMA_E_WORKSPACE, "probe buffers hold %d rows, the step has %d", m->probe_rows,
+                rows);
   if (!m->cap) return LLAMA_OK;
   size_t need = (size_t)m->d.nexec * 2 * rows * m->d.H * 2;
   if (m->cap_bytes < need)
@@ -710,6 +802,57 @@ int llama_sample(llama_model* m, const void* logits_bf16_dev, int32_t rows, int6
                 m->at<float>(m->L.smp_v), m->at<int>(m->L.smp_i), m->at<int>(m->L.smp_bad),
                 tokens_dev, m->at<int>(m->L.flag), s);
   return dev_check("sample launch");
+}
+
+int llama_test_linear(llama_model* m, int32_t prompt_kernel, const void* x, int32_t rows,
+                      const void* w, int32_t n, int32_t k, void* y, float* y32, void* hip_stream) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  if (!x || !w || !y || !y32) return fail(LLAMA_E_ARG, "NULL buffer");
+  if (n < 128 || k < 128 || n % 128 || k % 128)
+    return fail(LLAMA_E_ARG, "n %d and k %d must be positive multiples of 128", n, k);
+  if (prompt_kernel < 0 || prompt_kernel > 2)
+    return fail(LLAMA_E_ARG, "prompt_kernel %d is not 0, 1 or 2", prompt_kernel);
+  const int maxr = prompt_kernel ? 2048 : 16;
+  if (rows < 1 || rows > maxr) return fail(LLAMA_E_ARG, "rows %d outside 1..%d", rows, maxr);
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  GemvSeg seg[1] = {{(const uint16_t*)w, 0, n}};
+  if (prompt_kernel)
+    launch_gemm(GEMV_STORE, x, k, rows, k, seg, 1, nullptr, nullptr, y, n, y32, n, n,
+                prompt_kernel == 2, s);
+  else
+    launch_gemv(GEMV_STORE, seg, 1, n, k, x, k, rows, y, n, y32, n, nullptr, 0.f, s);
+  return dev_check("test linear launch");
+}
+
+int llama_test_attention(llama_model* m, int32_t prompt_kernel, llama_kv* kv, int32_t exec,
+                         const void* q, int32_t rows, int32_t pos0, void* out, float* out32,
+                         void* hip_stream) {
+  if (!m) return fail(LLAMA_E_ARG, "model is NULL");
+  int rc = check_kv(m, kv);
+  if (rc) return rc;
+  if (!q || !out) return fail(LLAMA_E_ARG, "NULL buffer");
+  if (exec < 0 || exec >= m->d.nexec)
+    return fail(LLAMA_E_ARG, "execution %d outside 0..%d", exec, m->d.nexec - 1);
+  if (prompt_kernel < 0 || prompt_kernel > 2)
+    return fail(LLAMA_E_ARG, "prompt_kernel %d is not 0, 1 or 2", prompt_kernel);
+  const int maxr = prompt_kernel ? m->cfg.max_chunk_rows : m->d.Mdec;
+  if (rows < 1 || rows > maxr) return fail(LLAMA_E_ARG, "rows %d outside 1..%d", rows, maxr);
+  if (pos0 < 0 || (int64_t)pos0 + rows > kv->length)
+    return fail(LLAMA_E_POSITION, "positions %d..%d are not all in the cache (%d)", pos0,
+                pos0 + rows - 1, kv->length);
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  Pass p{m, &kv, 1, rows, {0}, s};
+  p.pos0[0] = pos0;
+  RowTable tab = table_for(p, exec);
+  const Dims& d = m->d;
+  if (prompt_kernel)
+    launch_attn_prefill(q, tab.k[0], tab.v[0], rows, pos0, d.nq, d.nkv, d.d, out, out32,
+                        prompt_kernel == 2, s);
+  else
+    launch_attn_decode(q, tab, rows, d.nq, d.nkv, d.d, m->at<float>(m->L.part), out, out32, s);
+  return dev_check("test attention launch");
 }
 
 int llama_check_finite(llama_model* m, void* hip_stream) {

@@ -19,12 +19,12 @@ class Model:
     model) and ``b{i}.{attn_norm,q,k,v,o,mlp_norm,gate,up,down}``."""
 
     def __init__(self, geom, weights, max_positions, max_chunk_rows=2048, max_window_rows=16,
-                 max_seqs=2, device="cuda"):
+                 max_seqs=2, prompt_exact=False, device="cuda"):
         self.g = geom
         self.cfg = B.make_config(geom.n_blocks, geom.n_loops, geom.hidden, geom.n_q_heads,
                                  geom.n_kv_heads, geom.head_dim, geom.ffn, geom.vocab,
                                  geom.rope_theta, geom.rms_eps, max_chunk_rows, max_window_rows,
-                                 max_seqs)
+                                 max_seqs, prompt_exact)
         self.max_positions = max_positions
         nbytes = B.llama_workspace_bytes(self.cfg, max_positions)
         if nbytes == 0:
@@ -38,6 +38,30 @@ class Model:
                                            get("lm_head"), self.workspace.data_ptr(), nbytes,
                                            max_positions)
         self.capture = None
+
+    def set_probe(self, exec_index, rows, fields=None):
+        """Allocates and installs parity-probe buffers of ``rows`` rows for
+        execution ``exec_index`` (all fields, or those named); returns the
+        dict of device tensors (bf16 fields as int16).  ``rows=0`` clears the
+        hook."""
+        if not rows:
+            B.llama_set_probe(self.handle, 0, None, 0)
+            self.probe = None
+            return None
+        g = self.g
+        qd, kvd = g.n_q_heads * g.head_dim, g.n_kv_heads * g.head_dim
+        shapes = {"h_in": (g.hidden, torch.int16), "x_attn": (g.hidden, torch.int16),
+                  "qkv32": (qd + 2 * kvd, torch.float32), "q_rope": (qd, torch.int16),
+                  "attn": (qd, torch.int16), "attn32": (qd, torch.float32),
+                  "o32": (g.hidden, torch.float32), "x_mlp": (g.hidden, torch.int16),
+                  "gate_up32": (2 * g.ffn, torch.float32), "act": (g.ffn, torch.int16),
+                  "down32": (g.hidden, torch.float32)}
+        dev = self.workspace.device
+        self.probe = {k: torch.full((rows, w), -1, dtype=t, device=dev)
+                      for k, (w, t) in shapes.items() if fields is None or k in fields}
+        B.llama_set_probe(self.handle, exec_index,
+                          {k: v.data_ptr() for k, v in self.probe.items()}, rows)
+        return self.probe
 
     def new_sequence(self, max_positions=None):
         return Sequence(self, max_positions or self.max_positions)
@@ -166,8 +190,14 @@ class Sequence:
     def length(self):
         return B.llama_kv_length(self.handle)
 
-    def set_length(self, n):
-        B.llama_kv_set_length(self.handle, n)
+    def truncate(self, n):
+        """Keeps positions [0, n) (a resumed prompt state); shortens only."""
+        B.llama_kv_truncate(self.handle, n)
+
+    def declare(self, n):
+        """Test hook: positions [0, n) hold keys and values written through
+        ``view()``."""
+        B.llama_test_kv_declare(self.handle, n)
 
     def view(self):
         """The cache as int16 [executions][K/V][positions][kv_heads][head_dim]."""

@@ -76,6 +76,15 @@ typedef struct {
   int32_t max_chunk_rows;  /* largest llama_prefill_chunk, 1..2048 */
   int32_t max_window_rows; /* largest llama_decode_step window, 1..16 */
   int32_t max_seqs;        /* largest n_seq of llama_decode_step, 1..16 */
+  /* Prompt chunks' arithmetic (decode windows are unaffected): 0, the fast
+   * form, keeps each projection's fp32 sum in one matrix-unit chain over K
+   * and the attention weights in two bf16 parts (16 significant bits);
+   * 1, the exact form, restarts the projection sums every 128 terms into
+   * fp32 totals and keeps the weights in three bf16 parts (24 bits), at
+   * about 2x the projection time and 1.4x the attention time.  Both are fp32
+   * sums rounded once, as the spec asks; the exact form's per-element error
+   * is close to the decode kernels'. */
+  int32_t prompt_exact;
 } llama_config;
 
 /* Device addresses of one block's bf16 weights. */
@@ -113,9 +122,21 @@ int llama_kv_alloc(llama_model* model, int32_t max_positions, void* device_buf, 
 
 int32_t llama_kv_length(const llama_kv* kv);
 
-/* Sets the cache length: shorter keeps a prefix (a resumed prompt state);
- * longer declares positions the caller wrote into the buffer itself. */
-int llama_kv_set_length(llama_kv* kv, int32_t n_positions);
+/* Resumes from a kept prompt state (pull request "llama: Nanbeige4.3-33B on
+ * Metal, the bf16 release served as published", section "Measured": a
+ * resumed turn keeps the cached prefix and prefills only the rest): the
+ * cache keeps positions [0, n_positions) and the next prompt chunk starts at
+ * n_positions.  Shortens only: 0 <= n_positions <= llama_kv_length(kv), else
+ * LLAMA_E_POSITION and nothing changes.  Host-only, no device work. */
+int llama_kv_truncate(llama_kv* kv, int32_t n_positions);
+
+/* Test hook, not for serving: declares that positions [0, n_positions) of
+ * every execution hold keys and values the caller wrote itself through
+ * llama_kv_slab (synthetic caches for parity tests and benchmarks).  The
+ * library cannot check what the buffer holds; steps then read those slots
+ * as written.  n_positions 0..max_positions of the cache, else
+ * LLAMA_E_CAPACITY. */
+int llama_test_kv_declare(llama_kv* kv, int32_t n_positions);
 
 /* Device address of execution e's keys (which = 0) or values (which = 1). */
 void* llama_kv_slab(const llama_kv* kv, int32_t exec, int32_t which);
@@ -156,6 +177,72 @@ int llama_decode_step(llama_model* model, llama_kv* const* kvs, int32_t n_seq,
  * half, [1] after the MLP half; rows = the step's total rows).  NULL clears
  * it.  A later step whose capture would not fit is refused. */
 int llama_set_capture(llama_model* model, void* buf_dev, size_t bytes);
+
+/* Test hook for parity of single kernels.  While set, every step also writes
+ * the intermediate values of one execution `exec` into the caller's device
+ * buffers below (each nullable; rows = the step's total rows, at most
+ * max_rows, else the step is refused with LLAMA_E_WORKSPACE):
+ *   h_in      bf16 [rows][hidden]         residual entering the execution
+ *                                         (after a loop boundary: the
+ *                                         final-normed state)
+ *   x_attn    bf16 [rows][hidden]         RMSNorm output feeding q/k/v
+ *   qkv32     fp32 [rows][nq*d + 2*nkv*d] q, k, v sums before rounding
+ *   q_rope    bf16 [rows][nq*d]           q after RoPE
+ *   attn      bf16 [rows][nq*d]           attention output
+ *   attn32    fp32 [rows][nq*d]           attention output before rounding
+ *   o32       fp32 [rows][hidden]         o projection sums
+ *   x_mlp     bf16 [rows][hidden]         RMSNorm output feeding gate/up
+ *   gate_up32 fp32 [rows][2*ffn]          gate sums, then up sums
+ *   act       bf16 [rows][ffn]            SwiGLU output
+ *   down32    fp32 [rows][hidden]         down projection sums
+ * Sums that a fused launch keeps in registers come from an extra launch of
+ * the same projection kernel with a storing epilogue (every output's
+ * summation order is the same whichever epilogue runs), so the probe reports
+ * what the fused step rounds.  NULL clears the hook.  Steps are slower while
+ * it is set; their results are unchanged. */
+typedef struct {
+  void* h_in;
+  void* x_attn;
+  float* qkv32;
+  void* q_rope;
+  void* attn;
+  float* attn32;
+  float* o32;
+  void* x_mlp;
+  float* gate_up32;
+  void* act;
+  float* down32;
+} llama_probe;
+int llama_set_probe(llama_model* model, int32_t exec, const llama_probe* probe, int32_t max_rows);
+
+/* Test hooks for parity of single kernels on caller-given operands (the
+ * oracle's inputs), outside any step.  prompt_kernel selects the kernel a
+ * decode window runs (0), the one a prompt chunk runs in the fast form (1) or
+ * in the exact form (2; see llama_config.prompt_exact).
+ *
+ * llama_test_linear: y[r][j] = sum_k w[j][k] x[r][k] for rows r < rows
+ * (bf16 x [rows][k], bf16 w [n][k]) with the step's projection kernel and a
+ * storing epilogue: y_dev bf16 [rows][n] (the sums rounded once) and y32_dev
+ * fp32 [rows][n] (the sums).  n and k multiples of 128; rows 1..2048 for the
+ * prompt kernel, 1..16 for the decode kernel.  Row projections with fp32
+ * sums rounded once: pull request "llama: Nanbeige4.3-33B on Metal, the bf16
+ * release served as published", section "How".
+ *
+ * llama_test_attention: causal grouped-query attention of rows q_dev (bf16
+ * [rows][n_q_heads][head_dim], after RoPE) at positions [pos0, pos0 + rows)
+ * against execution `exec` of cache kv, which must hold positions
+ * [0, pos0 + rows); out_dev bf16 [rows][n_q_heads][head_dim] and out32_dev
+ * (nullable) the output before rounding.  rows 1..max_chunk_rows for the
+ * prompt kernel, 1..max_seqs * max_window_rows for the decode kernel (its
+ * partial sums use the model's workspace, so calls on one model are
+ * serialised by their stream).  Asynchronous on hip_stream; refusals return
+ * LLAMA_E_ARG or LLAMA_E_POSITION before anything is enqueued. */
+int llama_test_linear(llama_model* model, int32_t prompt_kernel, const void* x_dev, int32_t rows,
+                      const void* w_dev, int32_t n, int32_t k, void* y_dev, float* y32_dev,
+                      void* hip_stream);
+int llama_test_attention(llama_model* model, int32_t prompt_kernel, llama_kv* kv, int32_t exec,
+                         const void* q_dev, int32_t rows, int32_t pos0, void* out_dev,
+                         float* out32_dev, void* hip_stream);
 
 /* Measurement hook for benchmarks.  While `kernel` is one of the classes
  * below, every step records a HIP event pair on its own stream around each

@@ -49,7 +49,8 @@ def to_dev(a):
     return torch.from_numpy(a.copy()).cuda()
 
 
-def gpu_model(g, max_positions, max_chunk_rows=2048, max_window_rows=16, max_seqs=2, weights=None):
+def gpu_model(g, max_positions, max_chunk_rows=2048, max_window_rows=16, max_seqs=2, weights=None,
+              prompt_exact=False):
     import torch
 
     import dense_gqa_llama_amd as L
@@ -57,7 +58,7 @@ def gpu_model(g, max_positions, max_chunk_rows=2048, max_window_rows=16, max_seq
     w = weights if weights is not None else sd.weights(g)
     torch.cuda.synchronize()
     return L.Model(g, w, max_positions=max_positions, max_chunk_rows=max_chunk_rows,
-                   max_window_rows=max_window_rows, max_seqs=max_seqs)
+                   max_window_rows=max_window_rows, max_seqs=max_seqs, prompt_exact=prompt_exact)
 
 
 class HalfRunner:
@@ -66,8 +67,9 @@ class HalfRunner:
     attention half add exactly 0 (bf16(h + 0) = h), which isolates the MLP
     half; zeroing down_proj isolates the attention half."""
 
-    def __init__(self, g, dev_weights, max_positions, max_rows):
+    def __init__(self, g, dev_weights, max_positions, max_rows, prompt_exact=False):
         import torch
+        self.prompt_exact = prompt_exact
         self.g1 = dataclasses.replace(g, n_blocks=1, n_loops=1, vocab=0)
         self.dev = dev_weights
         self.maxp = max_positions
@@ -88,13 +90,13 @@ class HalfRunner:
             w["b0.o"] = self.zero_o
         rows = h_in.shape[0]
         m = L.Model(self.g1, w, max_positions=self.maxp, max_chunk_rows=self.max_rows,
-                    max_window_rows=16, max_seqs=1)
+                    max_window_rows=16, max_seqs=1, prompt_exact=self.prompt_exact)
         s = m.new_sequence(self.maxp)
         if pos0:
             v = s.view()
             v[0, 0, :pos0] = to_dev(np.ascontiguousarray(kc[:pos0]))
             v[0, 1, :pos0] = to_dev(np.ascontiguousarray(vc[:pos0]))
-            s.set_length(pos0)
+            s.declare(pos0)
         hin = to_dev(np.ascontiguousarray(h_in))
         if chunk is None:
             chunk = rows > 16
@@ -107,14 +109,19 @@ class HalfRunner:
         return h, (cache[0, 0], cache[0, 1])
 
 
-def half_report(tag, got, ref, h_in, gate=0.999):
-    """Logs plain and addend-scaled agreement; returns the addend fraction."""
+def half_report(tag, got, ref, h_in, gate="literal"):
+    """Logs the agreement of a half's residual output with the oracle's:
+    exact, within 2 bf16 steps at max(|got|, |ref|), and within 2 steps at the
+    larger addend of the residual add (the distance a rounding-scale change of
+    the added term can make).  Returns the first (gate "literal"), or the
+    second (gate "addend": the prompt chunks' fast form, whose matrix-unit
+    sums are measured per kernel; its literal figure is logged beside)."""
     plain, pw = parity.within_ulps(got, ref)
     frac, worst = parity.within_addend_ulps(got, ref, h_in)
     exact = float((got == ref).mean())
     log(f"{tag}: exact {exact:.5f}  within 2 steps {plain:.5f} (worst {pw:g})  "
         f"at the addend {frac:.5f} (worst {worst:g})")
-    return frac
+    return plain if gate == "literal" else frac
 
 
 def exec_inputs(g, embed_rows, caps, final_norm):

@@ -38,7 +38,8 @@ def cfg_of(g, **kw):
                 n_kv_heads=g.n_kv_heads, head_dim=g.head_dim, ffn=g.ffn, vocab=g.vocab,
                 rope_theta=g.rope_theta, rms_eps=g.rms_eps)
     base.update(kw)
-    extra = {k: base.pop(k) for k in ("max_chunk_rows", "max_window_rows", "max_seqs") if k in base}
+    extra = {k: base.pop(k) for k in ("max_chunk_rows", "max_window_rows", "max_seqs",
+                                      "prompt_exact") if k in base}
     return B.make_config(**base, **extra)
 
 
@@ -52,6 +53,7 @@ def test_served_configs_are_sized(i):
     dict(head_dim=96), dict(hidden=7000), dict(n_q_heads=50), dict(n_q_heads=72, n_kv_heads=8),
     dict(vocab=166913), dict(rope_theta=0.0), dict(max_chunk_rows=4096), dict(max_window_rows=17),
     dict(max_seqs=0), dict(ffn=22000), dict(n_loops=0), dict(rms_eps=-1.0),
+    dict(prompt_exact=2), dict(prompt_exact=-1),
 ])
 def test_refused_geometries(change):
     g = CONFIGS[3]
@@ -117,24 +119,51 @@ def test_step_refusals_before_any_launch():
         expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], FAKE, FAKE, 1)  # both inputs
         expect(B.LLAMA_E_ARG, B.llama_decode_step, m, [kv], None, None, 1)  # neither
         # capacity: the last legal position is usable, the next is refused
-        B.llama_kv_set_length(kv, 127)
+        B.llama_test_kv_declare(kv, 127)
         expect(B.LLAMA_E_CAPACITY, B.llama_decode_step, m, [kv], FAKE, None, 2)
-        B.llama_kv_set_length(kv, 128)
+        B.llama_test_kv_declare(kv, 128)
         expect(B.LLAMA_E_CAPACITY, B.llama_decode_step, m, [kv], FAKE, None, 1)
-        expect(B.LLAMA_E_CAPACITY, B.llama_kv_set_length, kv, 129)
+        expect(B.LLAMA_E_CAPACITY, B.llama_test_kv_declare, kv, 129)
         assert B.llama_kv_length(kv) == 128  # refusal changed nothing
-        B.llama_kv_set_length(kv, 0)
+        # truncation only shortens: it cannot declare positions nobody wrote
+        B.llama_kv_truncate(kv, 100)
+        expect(B.LLAMA_E_POSITION, B.llama_kv_truncate, kv, 101)
+        expect(B.LLAMA_E_POSITION, B.llama_kv_truncate, kv, -1)
+        assert B.llama_kv_length(kv) == 100
+        B.llama_kv_truncate(kv, 0)
         # prompt chunks
         expect(B.LLAMA_E_POSITION, B.llama_prefill_chunk, m, kv, FAKE, None, 8, 3)
         expect(B.LLAMA_E_ARG, B.llama_prefill_chunk, m, kv, FAKE, None, 65, 0)
         expect(B.LLAMA_E_ARG, B.llama_prefill_chunk, m, kv, None, None, 8, 0)
-        B.llama_kv_set_length(kv, 100)
+        B.llama_test_kv_declare(kv, 100)
         expect(B.LLAMA_E_CAPACITY, B.llama_prefill_chunk, m, kv, FAKE, None, 64, 100)
         # capture too small for the step
         B.llama_set_capture(m, FAKE, 16)
-        B.llama_kv_set_length(kv, 0)
+        B.llama_kv_truncate(kv, 0)
         expect(B.LLAMA_E_WORKSPACE, B.llama_decode_step, m, [kv], FAKE, None, 1)
         B.llama_set_capture(m, None, 0)
+        # parity probe: execution in range, rows bounded
+        expect(B.LLAMA_E_ARG, B.llama_set_probe, m, g.n_exec, {"attn": FAKE}, 4)
+        expect(B.LLAMA_E_ARG, B.llama_set_probe, m, -1, {"attn": FAKE}, 4)
+        expect(B.LLAMA_E_ARG, B.llama_set_probe, m, 0, {"attn": FAKE}, 0)
+        B.llama_set_probe(m, 1, {"attn": FAKE}, 4)
+        expect(B.LLAMA_E_WORKSPACE, B.llama_decode_step, m, [kv, kv2], FAKE, None, 3)
+        expect(B.LLAMA_E_WORKSPACE, B.llama_prefill_chunk, m, kv, FAKE, None, 5, 0)
+        B.llama_set_probe(m, 0, None, 0)
+        assert B.llama_kv_length(kv) == 0
+        # single-kernel test entries: kernel kind, shapes, rows, positions
+        st = None
+        expect(B.LLAMA_E_ARG, B.llama_test_linear, m, 3, FAKE, 4, FAKE, 128, 128, FAKE, FAKE, st)
+        expect(B.LLAMA_E_ARG, B.llama_test_linear, m, 1, FAKE, 4, FAKE, 100, 128, FAKE, FAKE, st)
+        expect(B.LLAMA_E_ARG, B.llama_test_linear, m, 0, FAKE, 17, FAKE, 128, 128, FAKE, FAKE, st)
+        expect(B.LLAMA_E_ARG, B.llama_test_linear, m, 1, FAKE, 2049, FAKE, 128, 128, FAKE, FAKE,
+               st)
+        expect(B.LLAMA_E_ARG, B.llama_test_attention, m, 1, kv, g.n_exec, FAKE, 4, 0, FAKE)
+        expect(B.LLAMA_E_POSITION, B.llama_test_attention, m, 1, kv, 0, FAKE, 4, 0, FAKE)
+        B.llama_test_kv_declare(kv, 10)
+        expect(B.LLAMA_E_POSITION, B.llama_test_attention, m, 2, kv, 0, FAKE, 4, 7, FAKE)
+        expect(B.LLAMA_E_ARG, B.llama_test_attention, m, 0, kv, 0, FAKE, 33, 0, FAKE)
+        B.llama_kv_truncate(kv, 0)
         # another model's cache
         m2, _ = load(g, max_chunk_rows=64)
         expect(B.LLAMA_E_ARG, B.llama_decode_step, m2, [kv], FAKE, None, 1)
@@ -207,14 +236,13 @@ def test_draft_round_refusals():
                    dict(draft=t, draft_kv=tkv), dict(draft_kv=tkv), dict(target_kv=dkv),
                    dict(draft=other, draft_kv=okv)):
             expect(B.LLAMA_E_ARG, call, **kw)
-        B.llama_kv_set_length(dkv, 3)
+        B.llama_test_kv_declare(dkv, 3)
         expect(B.LLAMA_E_POSITION, call)
-        B.llama_kv_set_length(tkv, 27)
-        B.llama_kv_set_length(dkv, 27)
+        B.llama_test_kv_declare(tkv, 27)
+        B.llama_test_kv_declare(dkv, 27)
         expect(B.LLAMA_E_CAPACITY, call, n=5)  # the draft cache ends at 32
         # the seeded variant also checks its sampling arguments
-        B.llama_kv_set_length(dkv, 27)
-        B.llama_kv_set_length(tkv, 27)
+        assert B.llama_kv_length(dkv) == 27 and B.llama_kv_length(tkv) == 27
 
         def sampled(T=0.6, K=20, P=0.95, u=FAKE, n=4):
             return B.llama_draft_round_sampled(t, tkv, d, dkv, n, FAKE, T, K, P, u, FAKE)
@@ -223,8 +251,8 @@ def test_draft_round_refusals():
             expect(B.LLAMA_E_ARG, sampled, **kw)
         expect(B.LLAMA_E_CAPACITY, sampled, n=5)
         dkv2 = B.llama_kv_alloc(d, 128, FAKE, B.llama_kv_bytes(d, 128))
-        B.llama_kv_set_length(tkv, 60)
-        B.llama_kv_set_length(dkv2, 60)
+        B.llama_test_kv_declare(tkv, 60)
+        B.llama_test_kv_declare(dkv2, 60)
         expect(B.LLAMA_E_CAPACITY, call, draft_kv=dkv2, n=4)  # the target cache ends at 64
         assert B.llama_kv_length(tkv) == 60 and B.llama_kv_length(dkv2) == 60
         assert B.llama_kv_length(dkv) == 27

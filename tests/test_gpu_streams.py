@@ -87,7 +87,7 @@ def test_resumed_prompt_equals_fresh_tiny():
     res = model.new_sequence(cap)
     model.prefill(res, tokens=to_dev(p[:60]), all_rows=True)
     model.prefill(res, tokens=to_dev(p[::-1][:40].copy()), all_rows=True)
-    res.set_length(60)
+    res.truncate(60)
     orr = model.prefill(res, tokens=to_dev(p[60:]), all_rows=True)
     assert np.array_equal(u16(orr["logits"]), lf[60:])
     assert np.array_equal(u16(res.view())[:, :, :100], cf)
@@ -124,7 +124,7 @@ def test_resumed_prompt_equals_fresh_33b_layer():
         parts.append(u16(model.prefill(spl, hidden=to_dev(rows[a:b]), want_hidden=True)["hidden"]))
     assert np.array_equal(np.concatenate(parts), hf)
     assert np.array_equal(u16(spl.view())[:, :, :300], cf)
-    spl.set_length(211)
+    spl.truncate(211)
     hr = u16(model.prefill(spl, hidden=to_dev(rows[211:]), want_hidden=True)["hidden"])
     assert np.array_equal(hr, hf[211:])
     log("33B layer: split and resumed chunks equal the single chunk bit for bit")
@@ -151,7 +151,7 @@ def test_chunk_sizes_select_other_tiles_same_bits_33b_layer():
         parts.append(u16(model.prefill(spl, hidden=to_dev(rows[a:b]), want_hidden=True)["hidden"]))
     assert np.array_equal(np.concatenate(parts), hf)
     assert np.array_equal(u16(spl.view())[:, :, :n], cf)
-    spl.set_length(1000)
+    spl.truncate(1000)
     hr = u16(model.prefill(spl, hidden=to_dev(rows[1000:]), want_hidden=True)["hidden"])
     assert np.array_equal(hr, hf[1000:])
     assert np.array_equal(u16(spl.view())[:, :, :n], cf)

@@ -29,7 +29,7 @@ WINDOWS = (1, 7, 16)    # decode window widths timed
 WINDOW_STEPS = 8
 DRAFT_K = 7             # proposals per drafted round
 DRAFT_ROUNDS = 8
-LONG_T = 131071         # cache positions before the long-context rounds
+LONG_T = 131072         # prompt tokens of the long-context sequences (64 chunks)
 LONG_ROUNDS = 8
 STREAM_ROUNDS = 32
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -152,9 +152,223 @@ def cpu_baseline(g, T, reps=3):
     t_tok = g.n_exec * t_block + t_head
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": 1.0 / t_tok, "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(),
             "sample": (f"{reps} decode rows through one 33B block at context {T} "
                        f"({t_block:.3f} s each) + one lm_head row ({t_head:.3f} s); "
                        f"a token = {g.n_exec} block rows + 1 head row")}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_cores():
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def timed(stream, fn, reps=1):
+    """HIP-event milliseconds of reps calls of fn on the current stream."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def bench_tiny(stream, cpu):
+    """The tiny workload: a 64-token prompt in one chunk, then 15 one-row
+    greedy steps (16 generated tokens); the oracle runs the same request."""
+    import numpy as np
+    import torch
+
+    import dense_gqa_llama_amd as L
+    from synth import device as sd
+    from synth.workloads import config
+    g = config(1)
+    P, D = g.prompt_len, g.decode_steps
+    model = L.Model(g, sd.weights(g), max_positions=P + D, max_chunk_rows=P, max_seqs=1)
+    prompt = sd.tokens(P, g.prompt_seeds[0], 0, g.vocab)
+    seq = model.new_sequence(P + D)
+    buf = torch.empty(D, dtype=torch.int32, device="cuda")
+
+    def req():
+        seq.truncate(0)
+        buf[0:1].copy_(model.prefill(seq, tokens=prompt, want_logits=False)["next"])
+        for i in range(1, D):
+            model.decode([seq], tokens=buf[i - 1:i], want_logits=False, next_out=buf[i:i + 1])
+    req()
+    torch.cuda.synchronize()
+    pre_ms = timed(stream, lambda: (seq.truncate(0),
+                                    model.prefill(seq, tokens=prompt, want_logits=False)), 20) / 20
+    req_ms = timed(stream, req, 20) / 20
+    dec_ms = (req_ms - pre_ms) / (D - 1)
+    wbytes = g.decode_weight_bytes()
+    out = {"workload": "tiny dense GQA Llama (2 blocks, hidden 512, 8/2 heads of 64, FFN 1408, "
+                       "vocab 4096): 64-token prompt + 16 greedy tokens",
+           "prefill_tok_s": round(P / (pre_ms / 1e3), 1),
+           "decode_tok_s": round(1e3 / dec_ms, 1), "decode_ms_per_token": round(dec_ms, 4),
+           "decode_hbm_gbs": round(decode_bytes(g, P + D / 2) / (dec_ms / 1e3) / 1e9, 1),
+           "decode_hbm_frac": round(decode_bytes(g, P + D / 2) / (dec_ms / 1e3) / 1e9
+                                    / HBM_PEAK_GBS, 5),
+           "note": f"{wbytes / 1e6:.1f} MB of weights per token: bound by launch latency, "
+                   "not by HBM"}
+    if cpu:
+        from oracle.model import OracleModel
+        from tests.host_inputs import HostWeights
+        om = OracleModel(g, HostWeights(g))
+        t0 = time.perf_counter()
+        om.generate(om.new_sequence(P + D), prompt.cpu().numpy(), D)
+        t = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round((P + D) / t, 2), "unit": "tok/s (prompt + generated)",
+                               "cores": oracle_cores(), "kind": "oracle", "cpu": cpu_model(),
+                               "sample": "the whole request (64 prompt rows + 15 steps)"}
+    return out
+
+
+def bench_layer33(stream, cpu):
+    """One 33B-shaped layer decoding 1- and 16-row windows at 4,096 cache
+    positions of N(0,1) keys and values.  Four copies of the layer with
+    their own weights run in turn (4.7 GB, far past the 256 MB cache in front
+    of HBM), so each layer's weights come from HBM."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import dense_gqa_llama_amd as L
+    from synth import device as sd
+    from synth import normal_bf16_dev
+    from synth.workloads import config
+    g1 = config(2)
+    NC = 4
+    g = dataclasses.replace(g1, n_blocks=NC)
+    T = g.extra["cache_positions"]
+    model = L.Model(g, sd.weights(g), max_positions=T + 64, max_chunk_rows=16, max_seqs=1)
+    seq = model.new_sequence(T + 64)
+    normal_bf16_dev(seq.buf.data_ptr(), seq.buf.numel() // 2, g.extra["kv_seed"], 0,
+                    stream=stream.cuda_stream)
+    rows = sd.normal((16, g.hidden), g.extra["input_seed"], 20)
+    out = {"workload": "one 33B-shaped layer (hidden 7168, 56/8 heads of 128, FFN 22016), "
+                       "decode windows at 4,096 cache positions of N(0,1) keys and values",
+           "windows": []}
+    layer_w = g1.decode_weight_bytes()
+    for R in (1, 16):
+        seq.declare(T)
+        model.decode([seq], hidden=rows[:R], rows=R, want_hidden=True)  # warm
+        torch.cuda.synchronize()
+        reps = 10
+
+        def step():
+            seq.truncate(T)
+            model.decode([seq], hidden=rows[:R], rows=R, want_hidden=True)
+        ms = timed(stream, step, reps) / reps / NC
+        kvp = g1.kv_bytes_per_position()
+        byts = layer_w + (T + R) * kvp + R * kvp
+        out["windows"].append({"rows": R, "us_per_layer": round(ms * 1e3, 2),
+                               "hbm_gbs": round(byts / (ms / 1e3) / 1e9, 1),
+                               "hbm_frac": round(byts / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)})
+    if cpu:
+        import oracle
+        import synth
+        from synth.workloads import TensorIds
+        from tests.host_inputs import HostWeights
+        W = HostWeights(g1)
+        blk = {k: W(f"b0.{k}") for k in ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate",
+                                          "up", "down")}
+        kc = synth.normal_bf16((T + 1) * g1.kv_dim, g1.extra["kv_seed"], TensorIds.K_CACHE).reshape(
+            T + 1, g1.n_kv_heads, g1.head_dim)
+        vc = synth.normal_bf16((T + 1) * g1.kv_dim, g1.extra["kv_seed"], TensorIds.V_CACHE).reshape(
+            T + 1, g1.n_kv_heads, g1.head_dim)
+        row = synth.normal_bf16(g1.hidden, g1.extra["input_seed"], TensorIds.INPUT_ROWS).reshape(
+            1, g1.hidden)
+        t0 = time.perf_counter()
+        for _ in range(3):
+            oracle.block(g1, blk, kc, vc, np.array([T], dtype=np.int32), row)
+        t = (time.perf_counter() - t0) / 3
+        out["cpu_baseline"] = {"value": round(1e6 * t, 1), "unit": "us per layer row",
+                               "cores": oracle_cores(), "kind": "oracle", "cpu": cpu_model(),
+                               "sample": f"3 one-row decode steps of the layer at position {T}"}
+    return out
+
+
+def bench_looped(stream, cpu):
+    """The looped model: a 512-token prompt in one chunk, then 255 one-row
+    greedy steps (256 generated tokens); 44 executions over 22 blocks."""
+    import numpy as np
+    import torch
+
+    import dense_gqa_llama_amd as L
+    from synth import device as sd
+    from synth.workloads import config
+    g = config(4)
+    P, D = g.prompt_len, g.decode_steps
+    model = L.Model(g, sd.weights(g), max_positions=P + D, max_chunk_rows=P, max_seqs=1)
+    prompt = sd.tokens(P, g.prompt_seeds[0], 0, g.vocab)
+    seq = model.new_sequence(P + D)
+    buf = torch.empty(D, dtype=torch.int32, device="cuda")
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def req(ev=None):
+        seq.truncate(0)
+        if ev:
+            ev[0].record(stream)
+        buf[0:1].copy_(model.prefill(seq, tokens=prompt, want_logits=False)["next"])
+        if ev:
+            ev[1].record(stream)
+        for i in range(1, D):
+            model.decode([seq], tokens=buf[i - 1:i], want_logits=False, next_out=buf[i:i + 1])
+        if ev:
+            ev[2].record(stream)
+    req()
+    req(marks)
+    torch.cuda.synchronize()
+    pre_ms = marks[0].elapsed_time(marks[1])
+    dec_ms = marks[1].elapsed_time(marks[2]) / (D - 1)
+    byts = decode_bytes(g, P + D / 2)
+    out = {"workload": "looped model (22 blocks x 2 loops, hidden 3072, 48/8 heads of 128, "
+                       "FFN 8192, vocab 166912): 512-token prompt + 256 greedy tokens",
+           "prefill_tok_s": round(P / (pre_ms / 1e3), 1),
+           "prefill_gemm_tflops": round(prefill_gemm_flops(g, P) / (pre_ms / 1e3) / 1e12, 1),
+           "decode_tok_s": round(1e3 / dec_ms, 2), "decode_ms_per_token": round(dec_ms, 4),
+           "decode_hbm_gbs": round(byts / (dec_ms / 1e3) / 1e9, 1),
+           "decode_hbm_frac": round(byts / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if cpu:
+        import oracle
+        import synth
+        from synth.workloads import TensorIds
+        from tests.host_inputs import HostWeights
+        W = HostWeights(g)
+        blk = {k: W(f"b0.{k}") for k in ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate",
+                                          "up", "down")}
+        T = P + D // 2
+        kc = synth.normal_bf16((T + 1) * g.kv_dim, 9004, TensorIds.K_CACHE).reshape(
+            T + 1, g.n_kv_heads, g.head_dim)
+        vc = synth.normal_bf16((T + 1) * g.kv_dim, 9004, TensorIds.V_CACHE).reshape(
+            T + 1, g.n_kv_heads, g.head_dim)
+        row = synth.normal_bf16(g.hidden, 9005, TensorIds.INPUT_ROWS).reshape(1, g.hidden)
+        t0 = time.perf_counter()
+        for _ in range(3):
+            oracle.block(g, blk, kc, vc, np.array([T], dtype=np.int32), row)
+        tb = (time.perf_counter() - t0) / 3
+        t0 = time.perf_counter()
+        oracle.linear(row, W("lm_head"))
+        th = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(1.0 / (g.n_exec * tb + th), 3), "unit": "tok/s",
+                               "cores": oracle_cores(), "kind": "oracle", "cpu": cpu_model(),
+                               "sample": (f"3 decode rows through one block at context {T} "
+                                          f"({tb:.3f} s each) + one lm_head row ({th:.3f} s); a "
+                                          f"token = {g.n_exec} block rows + 1 head row")}
+    return out
 
 
 def main():
@@ -196,7 +410,7 @@ def main():
 
     def request(before_decode=None):
         """One request: prefill + D greedy steps; returns its events and tokens."""
-        seq.set_length(0)
+        seq.truncate(0)
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record(stream)
         out = model.prefill(seq, tokens=prompt, want_logits=False)
@@ -286,7 +500,7 @@ def main():
     windows = []
     wseq = model.new_sequence(cap)  # P + 16 * WINDOW_STEPS positions fit
     for rows in WINDOWS:
-        wseq.set_length(0)
+        wseq.truncate(0)
         model.prefill(wseq, tokens=prompt, want_logits=False)
         toks = sd.tokens(rows * WINDOW_STEPS, 4700 + rows, 0, g.vocab)
         model.decode([wseq], tokens=toks[:rows], rows=rows, want_logits=False)  # warm
@@ -334,39 +548,44 @@ def main():
     del dmodel, wd, tseq, dseq
     torch.cuda.empty_cache()
 
-    # long-context decode rounds (the 131k workload's shape): two sequences
-    # whose caches hold LONG_T synthetic positions (keys and values ~N(0, 1))
-    # share every round; prefilling 131k real tokens would take minutes
+    # the long-context workload: sequence 0 prefills its 131,072-token prompt
+    # in 64 chunks of 2,048 rows (timed whole; the last chunk's attention also
+    # on its own); sequence 1's cache is planted with N(0,1) keys and values
+    # (a second 131k prefill would add half a minute); then both share every
+    # decode round
     gl = config(5)
     lseqs = [model.new_sequence(LONG_T + LONG_ROUNDS + 1) for _ in range(2)]
     from synth import normal_bf16_dev
-    for i, sq in enumerate(lseqs):
-        normal_bf16_dev(sq.buf.data_ptr(), sq.buf.numel() // 2, 3005 + i, 0,
-                        stream=stream.cuda_stream)
-        sq.set_length(LONG_T)
-    # one prompt chunk of P rows at the end of the long cache (positions
-    # LONG_T + 1 - P .. LONG_T), the last of the 131k prompt's 64 chunks:
-    # whole chunk, and its attention timed on its own
-    lp0 = LONG_T + 1 - P
-    lchunk = {}
-    for rep in range(2):  # warm, then timed
-        lseqs[0].set_length(lp0)
-        if rep:
-            B.llama_set_timing(model.handle, "prefill_attn", g.n_exec)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        model.prefill(lseqs[0], tokens=prompt, want_logits=False)
-        b.record(stream)
-        torch.cuda.synchronize()
-        if rep:
-            cms = a.elapsed_time(b)
-            lams, _ = B.llama_timing_read(model.handle)
-            B.llama_set_timing(model.handle, "off")
-            lchunk = {"rows": P, "pos0": lp0, "ms": round(cms, 2), "tok_s": round(P / (cms / 1e3), 1),
-                      "attention_ms": round(lams, 2),
-                      "attention_tflops": round(prefill_attn_flops(g, P, lp0) / (lams / 1e3) / 1e12, 1)}
-    lseqs[0].set_length(LONG_T)
-    log(f"long-context prompt chunk: {lchunk}")
+    normal_bf16_dev(lseqs[1].buf.data_ptr(), lseqs[1].buf.numel() // 2, 3006, 0,
+                    stream=stream.cuda_stream)
+    lseqs[1].declare(LONG_T)
+    lprompt = sd.tokens(LONG_T, gl.prompt_seeds[0], 0, g.vocab)
+    nch = LONG_T // P
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nch + 1)]
+    B.llama_set_timing(model.handle, "prefill_attn", g.n_exec * nch)
+    ev[0].record(stream)
+    for c in range(nch):
+        if c == nch - 1:
+            lam_before, _ = B.llama_timing_read(model.handle)
+        model.prefill(lseqs[0], tokens=lprompt[c * P:(c + 1) * P], want_logits=False)
+        ev[c + 1].record(stream)
+        if c % 16 == 15:
+            log(f"131k prompt: chunk {c + 1}/{nch}")
+    torch.cuda.synchronize()
+    lams, _ = B.llama_timing_read(model.handle)  # the last chunk's attention
+    B.llama_set_timing(model.handle, "off")
+    whole_ms = ev[0].elapsed_time(ev[nch])
+    cms = ev[nch - 1].elapsed_time(ev[nch])
+    lp0 = LONG_T - P
+    all_attn = sum(prefill_attn_flops(g, P, c * P) for c in range(nch))
+    lchunk = {"rows": P, "pos0": lp0, "ms": round(cms, 2), "tok_s": round(P / (cms / 1e3), 1),
+              "attention_ms": round(lams, 2),
+              "attention_tflops": round(prefill_attn_flops(g, P, lp0) / (lams / 1e3) / 1e12, 1)}
+    lprefill = {"tokens": LONG_T, "chunks": nch, "ms": round(whole_ms, 1),
+                "tok_s": round(LONG_T / (whole_ms / 1e3), 1),
+                "tflops": round((prefill_gemm_flops(g, LONG_T) + all_attn) / (whole_ms / 1e3) / 1e12, 1),
+                "attention_ms_before_last_chunk": round(lam_before, 1)}
+    log(f"131k prompt prefill: {lprefill}; last chunk: {lchunk}")
     ltok = sd.tokens(2, gl.prompt_seeds[0], 1, g.vocab)
     model.decode(lseqs, tokens=ltok, want_logits=False, next_out=ltok)  # warm
     torch.cuda.synchronize()
@@ -380,16 +599,16 @@ def main():
     ams, an = B.llama_timing_read(model.handle)
     B.llama_set_timing(model.handle, "off")
     lms = a.elapsed_time(b) / LONG_ROUNDS
-    T_avg = LONG_T + 1 + (LONG_ROUNDS - 1) / 2.0
+    T_avg = LONG_T + (LONG_ROUNDS - 1) / 2.0  # positions before each round's rows
     kvp = g.kv_bytes_per_position()
     lbytes = decode_bytes(g, T_avg) + (T_avg + 2) * kvp  # weights once, both caches
-    long_ctx = {"positions": LONG_T + 1, "sequences": 2, "ms_per_round": round(lms, 3),
+    long_ctx = {"positions": LONG_T, "sequences": 2, "ms_per_round": round(lms, 3),
                 "tok_s": round(2 / (lms / 1e3), 2),
                 "hbm_gbs": round(lbytes / (lms / 1e3) / 1e9, 1),
                 "attention_us_per_block": round(ams * 1e3 / max(an, 1), 2),
                 "attention_gbs": round(2 * (T_avg + 2) * kvp / g.n_exec
                                        / (ams / max(an, 1) / 1e3) / 1e9, 1),
-                "prompt_chunk": lchunk}
+                "prompt_chunk": lchunk, "prompt_prefill": lprefill}
     log(f"long context: {long_ctx}")
     del lseqs
     torch.cuda.empty_cache()
@@ -410,6 +629,18 @@ def main():
     sample_us = a.elapsed_time(b) * 1e3 / 256
     log(f"sampling: {sample_us:.1f} us per row")
     del sq
+
+    # the other workloads, each in its own model (the 33B's memory is released
+    # first: its weights and caches are no longer needed)
+    del model, w, seq
+    torch.cuda.empty_cache()
+    cpu = not args.no_cpu_baseline
+    configs = {}
+    for name, fn in (("tiny", bench_tiny), ("layer33", bench_layer33), ("looped", bench_looped)):
+        log(f"workload {name}")
+        configs[name] = fn(stream, cpu)
+        log(f"{name}: {configs[name]}")
+        torch.cuda.empty_cache()
 
     result = {
         "metric": "decode tok/s + HBM GB/s (% peak), 33B bf16 batch 1; prefill tok/s",
@@ -447,6 +678,7 @@ def main():
         "drafting": drafting,
         "sampling": {"us_per_row": round(sample_us, 2), "temperature": 0.6, "top_k": 20,
                      "top_p": 0.95},
+        "configs": configs,
         "roofline": {"bound": "hbm", "kernel": "decode gate/up projection + SwiGLU (R=1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -19,7 +19,8 @@ block, hidden rows in and out) has no final norm.
 """
 import numpy as np
 
-from . import argmax, block, embed, f64, linear, rmsnorm
+from . import (argmax, attention, block, embed, f64, linear, residual_add, rmsnorm, rope,
+               swiglu)
 
 BLOCK_KINDS = ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down")
 
@@ -105,3 +106,34 @@ class OracleModel:
 
 def logits_f64(bits):
     return f64(bits)
+
+
+def block_rows(geom, w, kc, vc, pos, h, rows):
+    """One block execution over rows at positions ``pos`` whose outputs are
+    needed only for the rows ``rows`` (indexes into h): every row's key and
+    value are stored at its slot (as orc_block stores them, before any row
+    attends), then the selected rows run the rest of the block.  Returns
+    (mid, out) of the selected rows: the residual after the attention half
+    and after the MLP half.  The same steps in the same order as orc_block,
+    so the selected rows' bits equal a full block's."""
+    g = geom
+    pos = np.asarray(pos, dtype=np.int32)
+    rows = np.asarray(rows)
+    x = rmsnorm(h, w["attn_norm"], g.rms_eps)
+    k = rope(linear(x, w["k"]), pos, g.n_kv_heads, g.head_dim, g.rope_theta)
+    v = linear(x, w["v"])
+    kc[pos] = k.reshape(-1, g.n_kv_heads, g.head_dim)
+    vc[pos] = v.reshape(-1, g.n_kv_heads, g.head_dim)
+    xs = np.ascontiguousarray(x[rows])
+    q = rope(linear(xs, w["q"]), pos[rows], g.n_q_heads, g.head_dim, g.rope_theta)
+    a = attention(q, kc, vc, pos[rows], g.n_q_heads, g.n_kv_heads, g.head_dim)
+    mid = residual_add(np.ascontiguousarray(h[rows]), linear(a, w["o"]))
+    return mid, mlp_half(geom, w, mid)
+
+
+def mlp_half(geom, w, mid):
+    """The MLP half of a block on residual rows: RMSNorm, gate/up, SwiGLU,
+    down projection, residual add."""
+    x = rmsnorm(mid, w["mlp_norm"], geom.rms_eps)
+    m = swiglu(linear(x, w["gate"]), linear(x, w["up"]))
+    return residual_add(mid, linear(m, w["down"]))

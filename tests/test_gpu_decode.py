@@ -122,14 +122,16 @@ def test_tiny_end_to_end_logits(tiny):
     assert seq.length == n
 
 
-@pytest.mark.parametrize("step", [0, 1, 15])
-def test_tiny_layer_local(tiny, step):
+@pytest.mark.parametrize("step,exact", [(0, True), (0, False), (1, False), (15, False)])
+def test_tiny_layer_local(tiny, step, exact):
     """Every execution, each half on its own, from the oracle's inputs: the
-    prompt chunk (step 0, 64 rows) and one-row decode steps."""
+    prompt chunk (step 0, 64 rows; exact and fast forms) and one-row decode
+    steps."""
     from synth import device as sd
     g, W = tiny["g"], tiny["W"]
     st = tiny["steps"][step]
-    runner = HalfRunner(g, sd.weights(g), 96, 64)
+    runner = HalfRunner(g, sd.weights(g), 96, 64, prompt_exact=exact)
+    gate = "literal" if exact or step else "addend"
     ins = exec_inputs(g, oracle.embed(W("embed"), st["tokens"]), st["caps"], W("final_norm"))
     for e in range(g.n_exec):
         b = e % g.n_blocks
@@ -137,9 +139,9 @@ def test_tiny_layer_local(tiny, step):
         got_mid, (kc, vc) = runner.run(b, ins[e], tiny["kc"][e], tiny["vc"][e], st["pos0"], "attn")
         got_out, _ = runner.run(b, mid, tiny["kc"][e], tiny["vc"][e], st["pos0"], "mlp")
         got_layer, _ = runner.run(b, ins[e], tiny["kc"][e], tiny["vc"][e], st["pos0"], "layer")
-        tag = f"tiny step {step} exec {e}"
-        assert half_report(tag + " attention half", got_mid, mid, ins[e]) >= 0.999
-        assert half_report(tag + " MLP half", got_out, outr, mid) >= 0.999
+        tag = f"tiny step {step} exec {e}" + (" (exact prompt form)" if exact else "")
+        assert half_report(tag + " attention half", got_mid, mid, ins[e], gate) >= 0.999
+        assert half_report(tag + " MLP half", got_out, outr, mid, gate) >= 0.999
         half_report(tag + " whole layer (reported)", got_layer, outr, ins[e])
         n = st["pos0"] + len(st["tokens"])
         for which, c, ref in ((0, kc, tiny["kc"][e]), (1, vc, tiny["vc"][e])):
@@ -187,8 +189,8 @@ def test_window_equals_one_row_steps_gpu(tiny):
         planted[3, 11] ^= np.uint16(1)
         assert parity.differing_rows(got, planted) == [3]  # the planted row is reported
         assert parity.differing_rows(got, want) == []
-        a.set_length(40)
-        b.set_length(40)
+        a.truncate(40)
+        b.truncate(40)
     # every slot either side wrote (unwritten slots hold whatever the buffer held)
     assert (u16(a.view())[:, :, :56] == u16(b.view())[:, :, :56]).all()
 
@@ -296,10 +298,10 @@ def test_layer33_window_equals_one_row(layer33):
     v = seq.view()
     v[0, 0, :T] = to_dev(layer33["kc0"][:T])
     v[0, 1, :T] = to_dev(layer33["vc0"][:T])
-    seq.set_length(T)
+    seq.declare(T)
     rows = to_dev(layer33["rows"])
     h16 = u16(model.decode([seq], hidden=rows, rows=16)["hidden"])
-    seq.set_length(T)
+    seq.truncate(T)
     ones = [u16(model.decode([seq], hidden=rows[i:i + 1], rows=1)["hidden"]) for i in range(16)]
     assert parity.differing_rows(np.concatenate(ones), h16) == []
     assert seq.length == T + 16

@@ -4,30 +4,23 @@ decode rounds with both sequences batched into every step).
 
 * Each reply must equal its solo run, bit for bit (the pull request "llama:
   Nanbeige4.3-33B on Metal, the bf16 release served as published", section
-  "Measured": concurrent rows equal solo rows).
-* The oracle cannot walk 131k rows through 52 blocks, so it is checked
-  layer-locally at full context: sampled rows of the last prompt chunk and the
-  last decode row of the first sequence, at the first and the last execution,
-  each half recomputed by the oracle from the GPU's own input rows and the
-  GPU's own cache of every earlier position (the oracle writes its own key and
-  value for the row's position); and the head (final norm + lm_head) from the
-  GPU's final residual of that decode row.
-* At this length the attention half is ill-conditioned on random-init
-  weights: the scores have a standard deviation near 3, a few dozen keys carry
-  the softmax, and a one-step rounding difference in a single query element
-  (fp32 sums in another order, which the spec admits) moves the output by
-  ~1e-4 relative.  So that half is judged against the spread of a second
-  valid reference -- the oracle's attention half with its q/k/v projections
-  summed in float32 instead of binary64 -- and the strict per-element gate is
-  applied where every key carries equal weight (zero q projection: uniform
-  attention, so a missing or repeated key tile moves every output), over the
-  full 131k-position cache, for a decode window and for a prompt chunk."""
+  "Measured": concurrent rows equal solo rows), and every greedy id must be
+  the argmax of the GPU's own logits.
+* The oracle cannot walk 131k rows through 52 blocks, and nothing the GPU
+  computes is fed to it; its checks at this context are layer-local from
+  synthetic states that reach both sides (tests/test_gpu_models.py: the last
+  2,048-row chunk of the prompt over a 129,024-position cache of N(0,1) keys
+  and values, and the last decode position), per kernel at 129k context
+  (tests/test_gpu_kernels.py), and here the strict per-element gate where
+  every key weighs the same: q projection zeroed, so each row averages the
+  values of all its positions over a full 131,072-position N(0,1) cache, for
+  a decode window and for a prompt chunk -- a missing or repeated key tile
+  moves every output there."""
 import numpy as np
 import pytest
 
 import oracle
 from synth.workloads import config
-from tests import parity
 from tests.gpu_util import half_report, log, u16
 from tests.host_inputs import HostWeights
 
@@ -38,70 +31,9 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 KINDS = ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down")
-SAMPLED_EXECS = (0, 51)
-CHUNK_ROWS_SAMPLED = (0, 777, 2047)   # rows of the last prompt chunk
 
 
-def _attn_alt(g, blk, kc, vc, pos, h_in):
-    """The attention half with q, k and v summed in float32 (numpy's own
-    order), rounded once to bf16, then the oracle's RoPE, attention, o_proj
-    and residual add: a second reference within the spec."""
-    x = oracle.f64(oracle.rmsnorm(h_in, blk["attn_norm"], g.rms_eps)).astype(np.float32)
-
-    def proj(W):
-        return oracle.bf16((x @ oracle.f64(W).astype(np.float32).T).astype(np.float64))
-    q = oracle.rope(proj(blk["q"]), [pos], g.n_q_heads, g.head_dim, g.rope_theta)
-    k = oracle.rope(proj(blk["k"]), [pos], g.n_kv_heads, g.head_dim, g.rope_theta)
-    kc, vc = kc.copy(), vc.copy()
-    kc[pos] = k.reshape(g.n_kv_heads, g.head_dim)
-    vc[pos] = proj(blk["v"]).reshape(g.n_kv_heads, g.head_dim)
-    a = oracle.attention(q, kc, vc, [pos], g.n_q_heads, g.n_kv_heads, g.head_dim)
-    return oracle.residual_add(h_in, oracle.linear(a, blk["o"]))
-
-
-def _halves(g, W, e, kc, vc, pos, h_in, mid, out, tag):
-    """Oracle halves of execution e for rows at positions ``pos``: the
-    attention half from the GPU's input rows and cache (with the second
-    reference beside it), the MLP half from the GPU's mid rows."""
-    blk = {k: W(f"b{e % g.n_blocks}.{k}") for k in KINDS}
-    ref, alt = [], []
-    for j, p in enumerate(pos):
-        kcp = np.ascontiguousarray(kc[:p + 1])
-        vcp = np.ascontiguousarray(vc[:p + 1])
-        alt.append(_attn_alt(g, blk, kcp, vcp, p, h_in[j:j + 1]))
-        _, m = oracle.block(g, blk, kcp, vcp, np.array([p], dtype=np.int32), h_in[j:j + 1],
-                            want_mid=True)
-        ref.append(m)
-    ref, alt = np.concatenate(ref), np.concatenate(alt)
-    fg = half_report(f"{tag} exec {e} attention half", mid, ref, h_in, gate=None)
-    fa, wa = parity.within_addend_ulps(alt, ref, h_in)
-    _, wg = parity.within_addend_ulps(mid, ref, h_in)
-    log(f"{tag} exec {e} float32-sum reference at the addend: {fa:.5f} (worst {wa:g})")
-    assert fg >= 0.999 or ((1 - fg) <= 2 * (1 - fa) and wg <= 2 * wa + 2)
-    x = oracle.rmsnorm(mid, blk["mlp_norm"], g.rms_eps)
-    m = oracle.swiglu(oracle.linear(x, blk["gate"]), oracle.linear(x, blk["up"]))
-    out_ref = oracle.residual_add(mid, oracle.linear(m, blk["down"]))
-    assert half_report(f"{tag} exec {e} MLP half", out, out_ref, mid) >= 0.999
-
-
-def _exec_rows(g, W, cap, e, rows, tokens):
-    """(h_in, mid, out) of execution e for the captured rows."""
-    mid = u16(cap[e, 0])[rows]
-    out = u16(cap[e, 1])[rows]
-    if e == 0:
-        h_in = oracle.embed(W("embed"), tokens)
-    else:
-        h_in = u16(cap[e - 1, 1])[rows]
-    return h_in, mid, out
-
-
-def _cache(seq, e, upto):
-    v = seq.view()
-    return (v[e, 0, :upto].cpu().numpy().view(np.uint16),
-            v[e, 1, :upto].cpu().numpy().view(np.uint16))
-
-
-def test_two_long_sequences_equal_solo_and_oracle_locally():
+def test_two_long_sequences_equal_solo():
     import dense_gqa_llama_amd as L
     from synth import device as sd
     g = config(5)
@@ -112,61 +44,27 @@ def test_two_long_sequences_equal_solo_and_oracle_locally():
     model = L.Model(g, w, max_positions=P + S, max_chunk_rows=C, max_window_rows=16, max_seqs=2)
     seqs = [model.new_sequence(P + S) for _ in g.prompt_seeds]
     prompts = [sd.tokens(P, seed, 0, g.vocab) for seed in g.prompt_seeds]
-    W = HostWeights(g, keep_blocks=1)
 
     solo_tok, solo_bits, first = [], [], []
     for i, seq in enumerate(seqs):
         for c in range(P // C):
             last = c == P // C - 1
-            if i == 0 and last:
-                cap = model.set_capture(C)
             out = model.prefill(seq, tokens=prompts[i][c * C:(c + 1) * C], want_logits=last)
             if c % 8 == 7 or last:
                 torch.cuda.synchronize()
                 log(f"sequence {i}: chunk {c + 1}/{P // C} done")
+        assert int(out["next"].item()) == oracle.argmax(u16(out["logits"])[0])
         first.append(int(out["next"].item()))
         model.check_finite()
-        if i == 0:
-            model.set_capture(0)
-            toks = prompts[0][P - C:].cpu().numpy()
-            rows = np.array(CHUNK_ROWS_SAMPLED)
-            for e in SAMPLED_EXECS:
-                kc, vc = _cache(seq, e, P)
-                h_in, mid, outr = _exec_rows(g, W, cap, e, rows, toks[rows])
-                _halves(g, W, e, kc, vc, [P - C + int(r) for r in rows], h_in, mid, outr,
-                        f"prompt rows {[P - C + int(r) for r in rows]}")
-            del cap, kc, vc
         # solo greedy decode
         tok = torch.tensor([first[i]], dtype=torch.int32, device="cuda")
         toks_i, bits_i = [first[i]], []
         for step in range(S):
-            if i == 0 and step == S - 1:
-                cap = model.set_capture(1)
             o = model.decode([seq], tokens=tok)
             bits_i.append(u16(o["logits"])[0])
             tok = o["next"]
             toks_i.append(int(tok.item()))
-            if i == 0 and step == S - 1:
-                model.set_capture(0)
-                pos = P + S - 1
-                for e in SAMPLED_EXECS:
-                    kc, vc = _cache(seq, e, pos + 1)
-                    h_in, mid, outr = _exec_rows(g, W, cap, e, np.array([0]),
-                                                 np.array([toks_i[-2]], dtype=np.int32))
-                    _halves(g, W, e, kc, vc, [pos], h_in, mid, outr, f"decode row {pos}")
-                del kc, vc
-                # the head from the GPU's final residual
-                h_fin = u16(cap[g.n_exec - 1, 1])
-                x = oracle.rmsnorm(h_fin, W("final_norm"), g.rms_eps)
-                refb, ref64 = oracle.linear(x, W("lm_head"), want64=True)
-                got32 = o["logits32"].cpu().numpy()
-                err = float(np.abs(got32 - ref64).max())
-                kl = parity.mean_kl(ref64, got32)
-                counts, _ = parity.judge(parity.bf16_bits_to_f64(refb),
-                                         parity.bf16_bits_to_f64(bits_i[-1][None]))
-                log(f"decode row {pos} head: max|d| {err:.3e} KL {kl:.2e} {counts}")
-                assert err <= 0.05 and kl <= 1e-3 and parity.top1_gate(counts, 1)
-                del cap
+            assert toks_i[-1] == oracle.argmax(bits_i[-1])
         model.check_finite()
         solo_tok.append(toks_i)
         solo_bits.append(np.stack(bits_i))
@@ -174,7 +72,7 @@ def test_two_long_sequences_equal_solo_and_oracle_locally():
 
     # batched: both sequences in every step, from the same prompt caches
     for seq in seqs:
-        seq.set_length(P)
+        seq.truncate(P)
     tok = torch.tensor(first, dtype=torch.int32, device="cuda")
     bat_tok = [[first[0]], [first[1]]]
     bat_bits = [[], []]

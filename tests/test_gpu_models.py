@@ -1,19 +1,29 @@
-"""GPU parity at the full model sizes, sampled.  The GPU runs the launch
-configuration the benchmark times -- a whole prompt chunk (2,048 rows for the
-33B shape, 512 for the looped model) -- and, because attention is causal, its
-first rows are comparable with the oracle's forward of those rows alone.  The
-oracle walks the blocks one at a time with weights generated on the host (as
-the float64 reference in the pull request "llama: Nanbeige4.3-33B on Metal,
-the bf16 release served as published" ran one layer's weights at a time).
+"""GPU parity at the full model sizes.
 
-Deep random-init stacks amplify rounding: a one-step change of a single
-embedding element moves the oracle's own 33B logits by up to ~0.4.  So the
-tolerance gates here are layer-local -- sampled executions per half, and the
-head (final norm + lm_head) fed the oracle's final residual through an
-identity block -- while end to end the greedy choices must agree, every miss a
-near-tie or within the position's noise floor (how far the oracle's own logits
-move when the first row's input is moved by one bf16 step), and the logit
-distance is reported beside that floor."""
+1. Layer-local at the benchmark's shapes: executions of the 33B-shaped and
+   the looped model (first, middle, last block) run as a whole prompt chunk
+   of 2,048 / 512 rows -- the projection tiling and attention grid that the
+   benchmark times -- and as a one-row step at the workload's last decode
+   position, from synthetic states that reach the GPU and the oracle alike
+   (N(0,1) rows, caches of N(0,1) keys and values), >= 16 sampled rows spread
+   over the chunk down to the last compared per half; the long-context
+   workload's last prompt chunk over a 129,024-position cache likewise.  The
+   exact prompt form is held to 2 bf16 steps at max(|a|, |b|) on >= 99.9% of
+   elements; the fast form to 2 steps at the larger addend of the residual
+   add, its literal figure logged beside (its matrix-unit sums are measured
+   per kernel in tests/test_gpu_kernels.py).
+2. End to end: the oracle walks the first rows of the benchmark's prompt
+   through every block (one block's weights at a time, as the float64
+   reference in the pull request "llama: Nanbeige4.3-33B on Metal, the bf16
+   release served as published" did) and a few teacher-forced decode steps;
+   the GPU runs the whole chunk.  Deep random-init stacks amplify rounding: a
+   one-step change of the first row's embedding moves the oracle's own 33B
+   logits by ~0.7.  So the tight gates are layer-local (halves of sampled
+   executions, and the head fed the oracle's final residual through an
+   identity block), and end to end the GPU's greedy choices may differ from
+   the oracle's on no more rows than the oracle's own do under that one-step
+   change (and on at most one row when the nudged oracle has none).
+"""
 import numpy as np
 import pytest
 
@@ -104,6 +114,7 @@ def _run(cfg, sampled_execs):
 
     # 1. sampled executions, layer-local per half, as prompt chunks
     runner = HalfRunner(g, w, 64, 64)
+    runner_x = HalfRunner(g, w, 64, 64, prompt_exact=True)
     ins = exec_inputs(g, oracle.embed(W("embed"), ptoks[:SAMPLE_ROWS]), caps, W("final_norm"))
     empty = np.zeros((1, g.n_kv_heads, g.head_dim), dtype=np.uint16)
     for e in sampled_execs:
@@ -111,8 +122,14 @@ def _run(cfg, sampled_execs):
         mid, outr = caps[e]
         got_mid, _ = runner.run(b, ins[e], empty, empty, 0, "attn", chunk=True)
         got_out, _ = runner.run(b, mid, empty, empty, 0, "mlp", chunk=True)
-        assert half_report(f"config {cfg} exec {e} attention half", got_mid, mid, ins[e]) >= 0.999
-        assert half_report(f"config {cfg} exec {e} MLP half", got_out, outr, mid) >= 0.999
+        assert half_report(f"config {cfg} exec {e} attention half", got_mid, mid, ins[e],
+                           "addend") >= 0.999
+        assert half_report(f"config {cfg} exec {e} MLP half", got_out, outr, mid, "addend") >= 0.999
+        got_mid, _ = runner_x.run(b, ins[e], empty, empty, 0, "attn", chunk=True)
+        got_out, _ = runner_x.run(b, mid, empty, empty, 0, "mlp", chunk=True)
+        tag = f"config {cfg} exec {e} (exact prompt form)"
+        assert half_report(tag + " attention half", got_mid, mid, ins[e]) >= 0.999
+        assert half_report(tag + " MLP half", got_out, outr, mid) >= 0.999
 
     # 2. the head, layer-local
     err, kl, counts = _head_layer_local(g, w, h_out, ref64, refb)
@@ -148,13 +165,97 @@ def _run(cfg, sampled_execs):
     gotbf = np.concatenate([gotb, np.stack(dbf)])
     err = float(np.abs(got - all64).max())
     kl = parity.mean_kl(all64, got)
-    floors = np.abs(n64 - all64).max(axis=1)
-    counts, detail = parity.judge_with_floor(parity.bf16_bits_to_f64(allb),
-                                             parity.bf16_bits_to_f64(gotbf), floors)
-    log(f"config {cfg} end to end: logits max|d| {err:.3e} KL {kl:.2e} (reported); the oracle "
-        f"nudged by one step moves by up to {floors.max():.3e} (KL "
-        f"{parity.mean_kl(all64, n64):.2e}); judge {counts} {detail}")
-    assert parity.top1_gate(counts, all64.shape[0])
+    counts, detail = parity.judge(parity.bf16_bits_to_f64(allb), parity.bf16_bits_to_f64(gotbf))
+    ncounts, ndetail = parity.judge(parity.bf16_bits_to_f64(allb),
+                                    parity.bf16_bits_to_f64(oracle.bf16(n64)))
+    miss, nmiss = all64.shape[0] - counts["equal"], all64.shape[0] - ncounts["equal"]
+    log(f"config {cfg} end to end: logits max|d| {err:.3e} KL {kl:.2e}, judge {counts} {detail}; "
+        f"the oracle nudged by one step: max|d| {np.abs(n64 - all64).max():.3e} KL "
+        f"{parity.mean_kl(all64, n64):.2e}, judge {ncounts} {ndetail}")
+    assert miss <= max(1, nmiss)
+
+
+CHUNK_SAMPLE = (0, 1, 127, 128, 255, 256, 511, 640, 777, 1023, 1024, 1300, 1535, 1791, 2046, 2047)
+
+
+def _layer_local_at_shape(cfg, blocks, P, last_pos, exact, pos0=0):
+    """Executions of a workload at its benchmarked shapes from synthetic
+    states: a prompt chunk of P rows at positions pos0.. (over pos0 planted
+    positions of N(0,1) keys and values), >= 16 sampled rows spread over it
+    down to the last compared per half, and a one-row decode step at
+    last_pos over a planted cache."""
+    import synth
+    from oracle.model import block_rows, mlp_half
+    from synth import device as sd
+    from synth.workloads import TensorIds
+    g = config(cfg)
+    W = HostWeights(g, keep_blocks=1)
+    w = sd.weights(g)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({r for r in CHUNK_SAMPLE if r < P} | {P - 1}))
+    runner = HalfRunner(g, w, max(pos0 + P, last_pos + 1), P, prompt_exact=exact)
+    gate = "literal" if exact else "addend"
+    form = "exact" if exact else "fast"
+    for b in blocks:
+        blk = {k: W(f"b{b}.{k}") for k in ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate",
+                                            "up", "down")}
+        seed = 3600 + 10 * cfg + b
+        h = synth.normal_bf16(P * g.hidden, seed, TensorIds.INPUT_ROWS).reshape(P, g.hidden)
+        T = pos0 + P
+        kc = np.zeros((T, g.n_kv_heads, g.head_dim), dtype=np.uint16)
+        vc = np.zeros_like(kc)
+        if pos0:
+            kc[:pos0] = synth.normal_bf16(pos0 * g.kv_dim, seed, TensorIds.K_CACHE).reshape(
+                pos0, g.n_kv_heads, g.head_dim)
+            vc[:pos0] = synth.normal_bf16(pos0 * g.kv_dim, seed, TensorIds.V_CACHE).reshape(
+                pos0, g.n_kv_heads, g.head_dim)
+        mid, _ = block_rows(g, blk, kc, vc, np.arange(pos0, T, dtype=np.int32), h, rows)
+        got_mid, (gk, gv) = runner.run(b, h, kc, vc, pos0, "attn", chunk=True)
+        tag = (f"config {cfg} block {b}, {P}-row chunk at {pos0}, rows {rows[0]}..{rows[-1]}, "
+               f"{form} form")
+        assert half_report(tag + " attention half", got_mid[rows], mid, h[rows], gate) >= 0.999
+        for c, ref in ((gk[pos0:T], kc[pos0:]), (gv[pos0:T], vc[pos0:])):
+            assert parity.within_ulps(c, ref)[0] >= 0.999
+        del kc, vc, gk, gv
+        h2 = synth.normal_bf16(P * g.hidden, seed + 5, TensorIds.INPUT_ROWS).reshape(P, g.hidden)
+        got_out, _ = runner.run(b, h2, None, None, 0, "mlp", chunk=True)
+        out = mlp_half(g, blk, np.ascontiguousarray(h2[rows]))
+        assert half_report(tag + " MLP half", got_out[rows], out, h2[rows], gate) >= 0.999
+        if exact:  # the decode step does not depend on the prompt form
+            continue
+        # the last decode step's position, over a synthetic cache
+        T = last_pos
+        kcd = np.zeros((T + 1, g.n_kv_heads, g.head_dim), dtype=np.uint16)
+        vcd = np.zeros_like(kcd)
+        kcd[:T] = synth.normal_bf16(T * g.kv_dim, seed, TensorIds.K_CACHE).reshape(
+            T, g.n_kv_heads, g.head_dim)
+        vcd[:T] = synth.normal_bf16(T * g.kv_dim, seed, TensorIds.V_CACHE).reshape(
+            T, g.n_kv_heads, g.head_dim)
+        hd = synth.normal_bf16(g.hidden, seed + 7, TensorIds.INPUT_ROWS).reshape(1, g.hidden)
+        got_dmid, _ = runner.run(b, hd, kcd, vcd, T, "attn", chunk=False)
+        dmid, dout = block_rows(g, blk, kcd, vcd, np.array([T], dtype=np.int32), hd, [0])
+        got_dout, _ = runner.run(b, dmid, kcd, vcd, T, "mlp", chunk=False)
+        tag = f"config {cfg} block {b}, decode row at position {T}"
+        assert half_report(tag + " attention half", got_dmid, dmid, hd) >= 0.999
+        assert half_report(tag + " MLP half", got_dout, dout, dmid) >= 0.999
+
+
+@pytest.mark.parametrize("exact", [True, False])
+def test_33b_layers_at_benchmark_shape(exact):
+    _layer_local_at_shape(3, (0, 25, 51), 2048, 2175, exact)
+
+
+@pytest.mark.parametrize("exact", [True, False])
+def test_looped_layers_at_benchmark_shape(exact):
+    _layer_local_at_shape(4, (0, 11, 21), 512, 767, exact)
+
+
+@pytest.mark.parametrize("exact", [True, False])
+def test_long_context_layers_at_benchmark_shape(exact):
+    """The last 2,048-row chunk of a 131,072-token prompt (positions
+    129,024..131,071) and the last decode position of the workload (131,135),
+    first and last block."""
+    _layer_local_at_shape(5, (0, 51), 2048, 131135, exact, pos0=129024)
 
 
 def test_33b_full_model_sampled():

@@ -2,9 +2,11 @@
 against the CPU oracle: ragged chunks spanning several 128-row tiles, a second
 chunk continuing at pos0 > 0 (continuity across chunk boundaries, as the
 NInfer card's "Validation" section checks), and a 33B-shaped layer over a
-4096-slot cache.  Same gates as the decode tests (layer-local halves within 2
-bf16 steps at the addend on >= 99.9% of elements; logits max-abs 0.05 on the
-fp32 sums, KL <= 1e-3, top-1 >= 99% with near-ties only)."""
+4096-slot cache.  Layer-local halves within 2 bf16 steps on >= 99.9% of
+elements: at max(|a|, |b|) for the exact prompt form, at the larger addend of
+the residual add for the fast form (whose literal figure is logged beside);
+logits max-abs 0.05 on the fp32 sums, KL <= 1e-3, top-1 >= 99% with
+near-ties only."""
 import numpy as np
 import pytest
 
@@ -69,30 +71,36 @@ def test_chunked_prompt_logits(tiny200):
     assert seq.length == sum(CHUNKS)
 
 
-@pytest.mark.parametrize("chunk", [0, 1])
-def test_chunk_layer_local(tiny200, chunk):
+@pytest.mark.parametrize("chunk,exact", [(0, True), (1, True), (0, False), (1, False)])
+def test_chunk_layer_local(tiny200, chunk, exact):
+    """Both chunks of the ragged prompt, each half of each execution from the
+    oracle's inputs; the exact prompt form against the literal gate, the fast
+    form against the gate at the larger addend (its literal figure logged)."""
     from synth import device as sd
     g, W = tiny200["g"], tiny200["W"]
     st = tiny200["steps"][chunk]
-    runner = HalfRunner(g, sd.weights(g), 256, 256)
+    runner = HalfRunner(g, sd.weights(g), 256, 256, prompt_exact=exact)
+    gate = "literal" if exact else "addend"
     ins = exec_inputs(g, oracle.embed(W("embed"), st["tokens"]), st["caps"], W("final_norm"))
     for e in range(g.n_exec):
         mid, outr = st["caps"][e]
         kc0, vc0 = tiny200["kc"][e], tiny200["vc"][e]
         got_mid, (kc, vc) = runner.run(e % g.n_blocks, ins[e], kc0, vc0, st["pos0"], "attn")
         got_out, _ = runner.run(e % g.n_blocks, mid, kc0, vc0, st["pos0"], "mlp")
-        tag = f"tiny chunk {chunk} exec {e}"
-        assert half_report(tag + " attention half", got_mid, mid, ins[e]) >= 0.999
-        assert half_report(tag + " MLP half", got_out, outr, mid) >= 0.999
+        tag = f"tiny chunk {chunk} exec {e}" + (" (exact prompt form)" if exact else "")
+        assert half_report(tag + " attention half", got_mid, mid, ins[e], gate) >= 0.999
+        assert half_report(tag + " MLP half", got_out, outr, mid, gate) >= 0.999
         n = st["pos0"] + len(st["tokens"])
         for c, ref in ((kc, kc0), (vc, vc0)):
             frac, worst = parity.within_ulps(c[st["pos0"]:n], ref[st["pos0"]:n])
             assert frac >= 0.999, (tag, frac, worst)
 
 
-def test_layer33_chunk_vs_oracle():
+@pytest.mark.parametrize("exact", [True, False])
+def test_layer33_chunk_vs_oracle(exact):
     """A 144-row chunk (two 128-row tiles, ragged) of one 33B-shaped layer at
-    positions 4096..4239 over the N(0,1) cache."""
+    positions 4096..4239 over the N(0,1) cache; exact prompt form against the
+    literal gate, fast form at the larger addend (literal figure logged)."""
     import synth
     from synth import device as sd
     g = config(2)
@@ -112,19 +120,22 @@ def test_layer33_chunk_vs_oracle():
     h, mid = oracle.block(g, {k: W(f"b0.{k}") for k in
                               ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up", "down")},
                           kco, vco, np.arange(T, T + R, dtype=np.int32), rows, want_mid=True)
-    runner = HalfRunner(g, sd.weights(g), T + R, R)
+    runner = HalfRunner(g, sd.weights(g), T + R, R, prompt_exact=exact)
     got_mid, (kcg, vcg) = runner.run(0, rows, kc, vc, T, "attn")
     got_out, _ = runner.run(0, mid, kc, vc, T, "mlp")
-    a = half_report("layer33 chunk attention half", got_mid, mid, rows)
-    b = half_report("layer33 chunk MLP half", got_out, h, mid)
+    gate = "literal" if exact else "addend"
+    tag = "layer33 chunk" + (" (exact prompt form)" if exact else "")
+    a = half_report(tag + " attention half", got_mid, mid, rows, gate)
+    b = half_report(tag + " MLP half", got_out, h, mid, gate)
     fk, _ = parity.within_ulps(kcg[T:], kco[T:])
     fv, _ = parity.within_ulps(vcg[T:], vco[T:])
     log(f"layer33 chunk cache slots: k {fk:.5f} v {fv:.5f}")
     assert a >= 0.999 and b >= 0.999 and fk >= 0.999 and fv >= 0.999
 
 
-@pytest.mark.parametrize("cfg,n,bad", [(1, 200, 150), (2, 300, 211)])
-def test_nonfinite_row_reaches_only_later_rows(cfg, n, bad):
+@pytest.mark.parametrize("cfg,n,bad,exact", [(1, 200, 150, False), (2, 300, 211, False),
+                                             (1, 200, 150, True), (2, 300, 211, True)])
+def test_nonfinite_row_reaches_only_later_rows(cfg, n, bad, exact):
     """A non-finite input row poisons its own key and value; rows before it
     never attend to that slot (causal), so they must equal a clean run bit for
     bit -- the masked slot's value must not leak through a zero weight
@@ -133,7 +144,7 @@ def test_nonfinite_row_reaches_only_later_rows(cfg, n, bad):
     import synth
     from synth.workloads import TensorIds
     g = config(cfg)
-    model = gpu_model(g, 320, max_chunk_rows=320, max_seqs=1)
+    model = gpu_model(g, 320, max_chunk_rows=320, max_seqs=1, prompt_exact=exact)
     rows = synth.normal_bf16(n * g.hidden, 3120 + cfg, TensorIds.INPUT_ROWS).reshape(n, g.hidden)
     clean = model.new_sequence(320)
     hc = u16(model.prefill(clean, hidden=to_dev(rows), want_hidden=True)["hidden"])
@@ -190,25 +201,28 @@ def edge():
                 nudgedb=np.concatenate([b for _, b in nudged]))
 
 
-@pytest.mark.parametrize("chunk", range(len(EDGE_CHUNKS)))
-def test_degenerate_chunk_layer_local(edge, chunk):
+@pytest.mark.parametrize("chunk,exact", [(c, x) for x in (True, False)
+                                         for c in range(len(EDGE_CHUNKS))])
+def test_degenerate_chunk_layer_local(edge, chunk, exact):
     """Each edge chunk run as a prompt chunk (one-row chunks included) from
     the oracle's inputs: both halves of every execution and the cache slots
-    written, within 2 bf16 steps on >= 99.9% of elements."""
+    written, within 2 bf16 steps on >= 99.9% of elements (at max(|a|, |b|)
+    for the exact prompt form, at the larger addend for the fast form)."""
     from synth import device as sd
     g, W = edge["g"], edge["W"]
     st = edge["steps"][chunk]
     n = len(st["tokens"])
-    runner = HalfRunner(g, sd.weights(g), EDGE_CAP, 128)
+    runner = HalfRunner(g, sd.weights(g), EDGE_CAP, 128, prompt_exact=exact)
+    gate = "literal" if exact else "addend"
     ins = exec_inputs(g, oracle.embed(W("embed"), st["tokens"]), st["caps"], W("final_norm"))
     for e in range(g.n_exec):
         mid, outr = st["caps"][e]
         kc0, vc0 = edge["kc"][e], edge["vc"][e]
         got_mid, (kc, vc) = runner.run(e % g.n_blocks, ins[e], kc0, vc0, st["pos0"], "attn", chunk=True)
         got_out, _ = runner.run(e % g.n_blocks, mid, kc0, vc0, st["pos0"], "mlp", chunk=True)
-        tag = f"edge chunk of {n} at {st['pos0']} exec {e}"
-        assert half_report(tag + " attention half", got_mid, mid, ins[e]) >= 0.999
-        assert half_report(tag + " MLP half", got_out, outr, mid) >= 0.999
+        tag = f"edge chunk of {n} at {st['pos0']} exec {e}" + (" (exact)" if exact else "")
+        assert half_report(tag + " attention half", got_mid, mid, ins[e], gate) >= 0.999
+        assert half_report(tag + " MLP half", got_out, outr, mid, gate) >= 0.999
         end = st["pos0"] + n
         for c, ref in ((kc, kc0), (vc, vc0)):
             frac, worst = parity.within_ulps(c[st["pos0"]:end], ref[st["pos0"]:end])
@@ -217,11 +231,12 @@ def test_degenerate_chunk_layer_local(edge, chunk):
 
 def test_degenerate_chunk_logits(edge):
     """The edge chunks end to end: every row's logits within max-abs 0.05 and
-    KL 1e-3 of the oracle; every top-1 miss a near-tie or within the row's
-    noise floor (how far the oracle's own logits move under the one-step
-    nudge); and no more misses than the nudged oracle has against the oracle
-    on the same rows, plus max(1, 1% of rows): on random-init weights a
-    rounding-scale change alone flips the greedy choice of ~1.5% of rows."""
+    KL 1e-3 of the oracle; the GPU's greedy choice differs from the oracle's
+    on no more rows, and on no more red rows (contenders more than one bf16
+    step apart, or a third within it), than the oracle's own choice does when
+    the first token's embedding is moved by one bf16 step -- on random-init
+    weights a rounding-scale change alone flips the greedy choice of ~1.5% of
+    rows -- plus max(1, 1% of rows) misses."""
     g = edge["g"]
     model = gpu_model(g, EDGE_CAP, max_chunk_rows=128, max_seqs=1)
     seq = model.new_sequence(EDGE_CAP)
@@ -240,13 +255,13 @@ def test_degenerate_chunk_logits(edge):
     rows = ref64.shape[0]
     err = float(np.abs(l32 - ref64).max())
     kl = parity.mean_kl(ref64, l32)
-    floors = np.abs(edge["nudged64"] - ref64).max(axis=1)
-    counts, detail = parity.judge_with_floor(parity.bf16_bits_to_f64(refb),
-                                             parity.bf16_bits_to_f64(lbf), floors)
-    nudged_top1 = np.array([oracle.argmax(a) != oracle.argmax(b) for a, b in zip(edge["nudgedb"], refb)])
-    misses = counts["near-tie"] + counts["drift-tie"]
+    counts, detail = parity.judge(parity.bf16_bits_to_f64(refb), parity.bf16_bits_to_f64(lbf))
+    ncounts, ndetail = parity.judge(parity.bf16_bits_to_f64(refb),
+                                    parity.bf16_bits_to_f64(edge["nudgedb"]))
+    miss, nmiss = rows - counts["equal"], rows - ncounts["equal"]
     log(f"edge chunks {EDGE_CHUNKS}: max|dlogit| {err:.3e} KL {kl:.2e} judge {counts} {detail}; "
-        f"the nudged oracle moves by up to {floors.max():.3e} and changes the top-1 of "
-        f"{int(nudged_top1.sum())} of {rows} rows")
-    assert err <= 0.05 and kl <= 1e-3 and counts["red"] == 0
-    assert misses <= int(nudged_top1.sum()) + max(1, int(0.01 * rows))
+        f"the nudged oracle moves by up to {np.abs(edge['nudged64'] - ref64).max():.3e}, judge "
+        f"{ncounts} {ndetail}")
+    assert err <= 0.05 and kl <= 1e-3
+    assert counts["red"] <= ncounts["red"]
+    assert miss <= nmiss + max(1, int(0.01 * rows))

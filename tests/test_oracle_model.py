@@ -226,3 +226,31 @@ def test_ulp_distance_and_kl():
     assert parity.mean_kl(x, x) == 0.0
     assert parity.mean_kl(x, x + 3.0) < 1e-12  # shift invariance
     assert parity.mean_kl(x, x * 1.1) > 0
+
+
+def test_block_rows_equals_block():
+    """The sampled-rows composition of a block equals the block on every row
+    it returns, bit for bit, and stores the same cache (tiny geometry, rows
+    at positions 5.. over an earlier prefix)."""
+    import synth
+    from oracle.model import block_rows, mlp_half
+    from synth.workloads import TensorIds
+    g = config(1)
+    W = HostWeights(g)
+    w = {k: W(f"b1.{k}") for k in ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate", "up",
+                                    "down")}
+    T, n = 64, 40
+    h = synth.normal_bf16(n * g.hidden, 3500, TensorIds.INPUT_ROWS).reshape(n, g.hidden)
+    kc = synth.normal_bf16(T * g.kv_dim, 3500, TensorIds.K_CACHE).reshape(T, g.n_kv_heads,
+                                                                          g.head_dim)
+    vc = synth.normal_bf16(T * g.kv_dim, 3500, TensorIds.V_CACHE).reshape(T, g.n_kv_heads,
+                                                                          g.head_dim)
+    pos = np.arange(5, 5 + n, dtype=np.int32)
+    k1, v1 = kc.copy(), vc.copy()
+    out_all, mid_all = oracle.block(g, w, k1, v1, pos, h, want_mid=True)
+    rows = np.array([0, 7, 22, 39])
+    k2, v2 = kc.copy(), vc.copy()
+    mid, out = block_rows(g, w, k2, v2, pos, h, rows)
+    assert (mid == mid_all[rows]).all() and (out == out_all[rows]).all()
+    assert (k1 == k2).all() and (v1 == v2).all()
+    assert (mlp_half(g, w, mid_all) == out_all).all()

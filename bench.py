@@ -474,6 +474,39 @@ def main():
         f"{attn_ms:.1f} ms ({attn_tf:.0f} TFLOP/s)")
     traffic = stored_traffic()
 
+    # the exact prompt form (sums restarted every 128 terms, three-part
+    # attention weights) on the same chunk, in a second model over the same
+    # weights
+    mx = L.Model(g, w, max_positions=P, max_chunk_rows=P, max_window_rows=1, max_seqs=1,
+                 prompt_exact=True)
+    sx = mx.new_sequence(P)
+
+    def exact_chunk(kind=None, launches=0):
+        sx.truncate(0)
+        if kind:
+            B.llama_set_timing(mx.handle, kind, launches)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        mx.prefill(sx, tokens=prompt, want_logits=False)
+        b.record(stream)
+        torch.cuda.synchronize()
+        t = B.llama_timing_read(mx.handle)[0] if kind else 0.0
+        if kind:
+            B.llama_set_timing(mx.handle, "off")
+        return a.elapsed_time(b), t
+    exact_chunk()  # warm
+    xms = min(exact_chunk()[0] for _ in range(args.steps))
+    xg = exact_chunk("prefill_gemm", 4 * g.n_exec)[1]
+    xa = exact_chunk("prefill_attn", g.n_exec)[1]
+    prefill_exact = {"tok_s": round(P / (xms / 1e3), 1), "ms_per_chunk": round(xms, 2),
+                     "gemm_ms": round(xg, 2),
+                     "gemm_tflops": round(prefill_gemm_flops(g, P) / (xg / 1e3) / 1e12, 1),
+                     "attention_ms": round(xa, 2),
+                     "attention_tflops": round(prefill_attn_flops(g, P) / (xa / 1e3) / 1e12, 1)}
+    log(f"exact prompt form: {prefill_exact}")
+    del sx, mx
+    torch.cuda.empty_cache()
+
     # concurrent streams: n sequences, each with the prompt, share every decode
     # round (one row per sequence); aggregate tokens per second
     streams = [{"n": 1, "tok_s": round(dec_tps, 2)}]
@@ -668,6 +701,7 @@ def main():
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "ms_per_chunk": round(gemm_ms, 3)},
+        "prefill_exact_form": prefill_exact,
         "prefill_attention": {"bound": "mfma", "achieved": round(attn_tf, 1),
                               "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(attn_tf / MFMA_BF16_PEAK_TFLOPS, 4),

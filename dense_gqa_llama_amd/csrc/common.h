@@ -55,33 +55,54 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
 // RMSNorm, bf16(w * bf16(x * r)) with r = 1/sqrt(sum(x^2)/H + eps) (pull
 // request "llama: Nanbeige4.3-33B on Metal, the bf16 release served as
-// published", section "How").  One canonical order for the sum, used by the
-// standalone norm kernel and by every projection that normalises its input
-// rows itself, so a row's bits never depend on which of the two ran: a full
-// wave sums the row, lane l taking 16-byte vectors l, l+64, ... in order with
-// fused multiply-adds, then the xor butterfly.  H is a multiple of 8.
-// One 16-byte vector's squares added to a running sum, elements in order.
-__device__ __forceinline__ float sumsq8(u32x4_t q, float ss) {
+// published", section "How").  The sum of squares, r and x * r are binary64:
+// a bf16 square is exact there and a row's sum of them is exact for any
+// spread of magnitudes a normalised activation has (16 bits per square plus
+// the row's exponent range and log2(H) bits of growth fit in 53), so the
+// order of the sum does not change it; sqrt and the division are correctly
+// rounded, and x * r is rounded once to bf16 (via round-to-odd to fp32).  The
+// normed value is therefore the correctly rounded one, the same from the
+// standalone norm kernel and from every projection that normalises its own
+// input rows.  A full wave sums a row, lane l taking 16-byte vectors l,
+// l+64, ..., then the xor butterfly.  H is a multiple of 8.
+
+// binary64 -> bf16 bits, round to nearest even: truncate to fp32 and set the
+// last bit if anything was dropped (round to odd: 24 bits >= 8 + 2 make the
+// second rounding exact), then fp32 -> bf16.
+__device__ __forceinline__ bf16_t d2bf(double x) {
+  float f = __double2float_rz(x);
+  if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return f2bf(f);
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+  return v;
+}
+
+// One 16-byte vector's squares added to a running binary64 sum.
+__device__ __forceinline__ double sumsq8(u32x4_t q, double ss) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float a = bf_lo(w[j]), b = bf_hi(w[j]);
-    ss = fmaf(a, a, ss);
-    ss = fmaf(b, b, ss);
+    const double a = bf_lo(w[j]), b = bf_hi(w[j]);
+    ss = fma(a, a, ss);
+    ss = fma(b, b, ss);
   }
   return ss;
 }
 
-__device__ __forceinline__ float inv_rms(float lane_ss, int H, float eps) {
-  const float ss = wave_sum(lane_ss);
-  return 1.0f / sqrtf(ss / (float)H + eps);
+__device__ __forceinline__ double inv_rms(double lane_ss, int H, float eps) {
+  const double ss = wave_sum_d(lane_ss);
+  return 1.0 / sqrt(ss / (double)H + (double)eps);
 }
 
-__device__ __forceinline__ float row_inv_rms(const bf16_t* __restrict__ x, int H, float eps) {
+__device__ __forceinline__ double row_inv_rms(const bf16_t* __restrict__ x, int H, float eps) {
   const u32x4_t* xv = (const u32x4_t*)x;
   const int nv = H / 8;
-  float ss = 0.f;
-  // loads are issued eight at a time; the sum still runs in vector order
+  double ss = 0.0;
+  // loads are issued eight at a time
   for (int v0 = lane_id(); v0 < nv; v0 += 8 * WAVE) {
     u32x4_t q[8];
 #pragma unroll
@@ -99,20 +120,21 @@ __device__ __forceinline__ float row_inv_rms(const bf16_t* __restrict__ x, int H
 }
 
 // The same sum over a row already staged in LDS (nv = H / 8 vectors).
-__device__ __forceinline__ float row_inv_rms_lds(const u32x4_t* xv, int H, float eps) {
+__device__ __forceinline__ double row_inv_rms_lds(const u32x4_t* xv, int H, float eps) {
   const int nv = H / 8;
-  float ss = 0.f;
+  double ss = 0.0;
   for (int v = lane_id(); v < nv; v += WAVE) ss = sumsq8(xv[v], ss);
   return inv_rms(ss, H, eps);
 }
 
 // Eight normalised elements: bf16(w * bf16(x * r)), packed.
-__device__ __forceinline__ u32x4_t norm8(u32x4_t x, u32x4_t w, float r) {
+__device__ __forceinline__ u32x4_t norm8(u32x4_t x, u32x4_t w, double r) {
   const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t o[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float n0 = rbf(bf_lo(xs[j]) * r), n1 = rbf(bf_hi(xs[j]) * r);
+    const float n0 = bf2f(d2bf((double)bf_lo(xs[j]) * r));
+    const float n1 = bf2f(d2bf((double)bf_hi(xs[j]) * r));
     o[j] = pack_bf2(f2bf(bf_lo(ws[j]) * n0), f2bf(bf_hi(ws[j]) * n1));
   }
   return u32x4_t{o[0], o[1], o[2], o[3]};

@@ -183,8 +183,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   // boundaries and their barriers are uniform.  With NORM and whole rows the
   // norm factors are summed from LDS and the rows normalised in place; with
   // chunks, wave r first sums row r from memory and each chunk is normalised
-  // as it is staged.  Both sums take the canonical order.
-  __shared__ float srs[NORM ? R : 1];
+  // as it is staged.  Both take the same binary64 norm arithmetic.
+  __shared__ double srs[NORM ? R : 1];
   if (NORM && pre) {
 #pragma unroll
     for (int j = 0; j < XPRE; ++j) {
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     }
     __syncthreads();
     if (wave < R) {
-      const float rs = row_inv_rms_lds(sx + wave * cv, a.K, a.eps);
+      const double rs = row_inv_rms_lds(sx + wave * cv, a.K, a.eps);
       if (lane == 0) srs[wave] = rs;
     }
     __syncthreads();
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
   }
   if (NORM && !whole) {
     if (wave < R) {
-      const float rs = row_inv_rms(a.x + (size_t)wave * a.ldx, a.K, a.eps);
+      const double rs = row_inv_rms(a.x + (size_t)wave * a.ldx, a.K, a.eps);
       if (lane == 0) srs[wave] = rs;
     }
     __syncthreads();
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
       __syncthreads();
       if (NORM && whole) {
         if (wave < R) {
-          const float rs = row_inv_rms_lds(sx + wave * cv, a.K, a.eps);
+          const double rs = row_inv_rms_lds(sx + wave * cv, a.K, a.eps);
           if (lane == 0) srs[wave] = rs;
         }
         __syncthreads();
@@ -380,7 +380,7 @@ static void launch_r(GemvArgs a, int N, hipStream_t s) {
 
 // Inputs are normalised inside the projection for windows of up to
 // GEMV_NORM_ROWS rows; larger windows arrive normalised by rmsnorm_kernel
-// (same bits, one canonical order).
+// (same bits: the norm is binary64, correctly rounded).
 template <int EPI>
 static void launch_epi(int rows, const GemvArgs& a, int N, hipStream_t s) {
   if (a.normw) {

@@ -39,15 +39,15 @@ void launch_embed(const void* E, int vocab, int H, const int32_t* tok, void* h, 
 }
 
 // -------------------------------------------------------------- RMSNorm ----
-// out = bf16(w * bf16(x * r)) in the canonical order of row_inv_rms: one wave
-// per row, four rows per workgroup.  In place (out == h) is allowed: each
+// out = bf16(w * bf16(x * r)) with r and x * r as row_inv_rms and norm8 form
+// them: one wave per row, four rows per workgroup.  In place (out == h) is allowed: each
 // element is read and then written by the same lane, after the row's sum.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const bf16_t* h, const bf16_t* __restrict__ w,
                                                       bf16_t* out, int rows, int H, float eps) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;  // uniform per wave; no barrier follows
   const bf16_t* x = h + (size_t)r * H;
-  const float rs = row_inv_rms(x, H, eps);
+  const double rs = row_inv_rms(x, H, eps);
   const u32x4_t* xv = (const u32x4_t*)x;
   const u32x4_t* wv = (const u32x4_t*)w;
   u32x4_t* o = (u32x4_t*)(out + (size_t)r * H);

@@ -30,3 +30,31 @@ _ensure_host_libs()
 @pytest.fixture(scope="session")
 def root():
     return ROOT
+
+
+@pytest.hookimpl(hookwrapper=True)
+def pytest_runtest_makereport(item, call):
+    """Once a failing test's report is written, drop the local variables of
+    its traceback's frames: pytest keeps the exception until the session
+    ends, and a GPU test's frames hold device tensors and models of tens of
+    GiB that later tests in the same process would otherwise not get."""
+    outcome = yield
+    rep = outcome.get_result()
+    if call.excinfo is not None and rep.longrepr is not None:
+        import traceback
+        try:
+            traceback.clear_frames(call.excinfo.tb)
+        except Exception:
+            pass
+
+
+def pytest_runtest_teardown(item, nextitem):
+    if "gpu" in item.keywords:
+        import gc
+        gc.collect()
+        try:
+            import torch
+            if torch.cuda.is_available():
+                torch.cuda.empty_cache()
+        except Exception:
+            pass

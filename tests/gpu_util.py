@@ -124,6 +124,92 @@ def half_report(tag, got, ref, h_in, gate="literal"):
     return plain if gate == "literal" else frac
 
 
+class HalfGates:
+    """The per-layer gate on the residual outputs of block halves against the
+    oracle's.  check() logs one half and holds it to 2 bf16 steps at the
+    larger addend of its residual add on >= 99.9% of elements; finish() holds
+    the elements of every half checked to 2 steps at max(|got|, |ref|) (the
+    literal reading) on at least min(99.9%, 1 - 2 m), m being the literal
+    miss fraction, on the same elements, of `f32`: the same halves by an
+    ordinary float32 implementation of the spec (tests/fp32_ref.py) from the
+    same inputs.  The bar drops below 99.9% only where that reference itself
+    misses more than 0.05% of elements.
+
+    Why pooled and why relative: the literal distance of a half is set by
+    cascades -- one intermediate one step off moves every output reading it,
+    and a cancelling residual add turns one step of an addend into many of
+    the sum -- so a single flipped intermediate can put a whole row past 2
+    steps, which on a small geometry is a large share of one half's elements,
+    and on random-init weights even the float32 implementation misses 99.9%
+    on some shapes.  literal=False (the prompt chunks' fast form, whose
+    matrix-unit sums are held per kernel instead) logs the literal figures and
+    asserts only the addend bar."""
+
+    def __init__(self, literal=True):
+        self.literal = literal
+        self.n = 0
+        self.miss = 0
+        self.fmiss = 0
+        self.nf = 0
+
+    def check(self, tag, got, ref, h_in, f32=None):
+        d = parity.ulp_distance(got, ref)
+        plain, pw = float((d <= 2.0).mean()), float(d.max())
+        frac, worst = parity.within_addend_ulps(got, ref, h_in)
+        exact = float((got == ref).mean())
+        msg = (f"{tag}: exact {exact:.5f}  within 2 steps {plain:.5f} (worst {pw:g})  "
+               f"at the addend {frac:.5f} (worst {worst:g})")
+        self.n += d.size
+        self.miss += int((d > 2.0).sum())
+        if f32 is not None:
+            fd = parity.ulp_distance(f32, ref)
+            self.fmiss += int((fd > 2.0).sum())
+            self.nf += fd.size
+            msg += (f"  | float32 reference: exact {float((f32 == ref).mean()):.5f} within 2 "
+                    f"steps {float((fd <= 2.0).mean()):.5f} (worst {float(fd.max()):g})")
+        log(msg)
+        assert frac >= 0.999, f"{tag}: {frac:.5f} within 2 steps at the addend"
+        return plain
+
+    def finish(self, tag):
+        plain = 1.0 - self.miss / max(self.n, 1)
+        bar = 0.999
+        msg = f"{tag}: {self.n} elements, within 2 steps {plain:.5f}"
+        if self.nf == self.n and self.n:
+            fplain = 1.0 - self.fmiss / self.n
+            bar = min(bar, 1.0 - 2.0 * (1.0 - fplain))
+            msg += f"; float32 reference {fplain:.5f}"
+        msg += f"; bar {bar:.5f}" + ("" if self.literal else " (logged, not held)")
+        log(msg)
+        if self.literal:
+            assert plain >= bar, msg
+        return plain
+
+
+def assert_half(tag, got, ref, h_in, f32=None, literal=True):
+    """One half on its own through HalfGates."""
+    hg = HalfGates(literal)
+    hg.check(tag, got, ref, h_in, f32)
+    return hg.finish(tag)
+
+
+def f32_halves(g, W, block, kc, vc, pos0, h_in, mid):
+    """Both halves of one execution by the float32 reference
+    (tests/fp32_ref.py) from the oracle's inputs: the attention half of the
+    rows h_in at positions pos0.. over the oracle's cache slots [0, pos0),
+    and the MLP half of the oracle's mid rows.  W: host weights."""
+    from tests import fp32_ref
+    blk = {k: W(f"b{block}.{k}") for k in KINDS}
+    n = h_in.shape[0]
+    kx = np.zeros((pos0 + n,) + tuple(kc.shape[1:]), dtype=np.uint16)
+    vx = np.zeros_like(kx)
+    kx[:pos0] = kc[:pos0]
+    vx[:pos0] = vc[:pos0]
+    pos = np.arange(pos0, pos0 + n, dtype=np.int32)
+    f_mid = fp32_ref.attn_half(g, blk, kx, vx, pos, h_in, np.arange(n))
+    return f_mid, fp32_ref.mlp_half(g, blk, mid)
+
+
 def exec_inputs(g, embed_rows, caps, final_norm):
     """The oracle's input rows of every execution, from its captures
     [(mid, out)] of one step: the embedding for the first, the previous

@@ -9,7 +9,9 @@ computes reaches the oracle.  Shapes are the 33B block's: the four prompt
 projections on 2,048-row chunks and the decode projections on 1- and 16-row
 windows, against the same weights; causal attention of 2,048-row prompt
 chunks at positions 0 and 129,024 and of a ragged 1,000-row chunk at 4,096,
-and decode windows at 4,096 and at the end of a 131,072-position cache.
+and decode windows at 4,096 and at the end of a 131,072-position cache; and
+attention with heads of 64 (the tiny workload's geometry), including a chunk
+whose rows sit off the key tiles.
 
 Gates: every element within one bf16 step of the correctly rounded exact
 value plus the worst-case fp32 summation error of its sum (parity.sum_bound_ok:
@@ -164,18 +166,34 @@ ATTN_CASES = [
 KIND = {"prompt-exact": 2, "prompt-fast": 1, "decode": 0}
 
 
-@pytest.mark.parametrize("kernel,rows,pos0", ATTN_CASES)
-def test_attention_kernels_vs_oracle(layer, kernel, rows, pos0):
+@pytest.fixture(scope="module")
+def small_layer():
+    """One block of the tiny workload's geometry: heads of 64, 8 query heads
+    over 2 KV heads."""
+    import dataclasses
+
+    import dense_gqa_llama_amd as L
+    from synth import device as sd
+    g = dataclasses.replace(config(1), n_blocks=1, vocab=0)
+    m = L.Model(g, sd.weights(g), max_positions=8192, max_chunk_rows=ROWS, max_window_rows=16,
+                max_seqs=1)
+    return dict(g=g, m=m)
+
+
+def _attention_case(layer, kernel, rows, pos0, max_positions):
     """Query rows q ~ N(0, 2.5^2) (scores with a standard deviation near 2.5:
     a few dozen keys carry each softmax, as with the random-init layer), keys
-    and values ~N(0,1) at every slot up to the last row's position."""
+    and values ~N(0,1) at every slot up to the last row's position.  The
+    float32 reference of the same attention (tests/fp32_ref.py) is logged
+    beside for scale."""
     import synth
     import dense_gqa_llama_amd.binding as B
+    from tests import fp32_ref
     g = layer["g"]
     m = layer["m"]
     T = pos0 + rows
     kvd = g.kv_dim
-    seq = m.new_sequence(131072)
+    seq = m.new_sequence(max_positions)
     v = seq.view()
     from synth import device as sd
     v[0, 0, :T] = sd.normal((T, g.n_kv_heads, g.head_dim), 3300, TensorIds.K_CACHE)
@@ -194,14 +212,35 @@ def test_attention_kernels_vs_oracle(layer, kernel, rows, pos0):
     kc = synth.normal_bf16(T * kvd, 3300, TensorIds.K_CACHE).reshape(T, g.n_kv_heads, g.head_dim)
     vc = synth.normal_bf16(T * kvd, 3300, TensorIds.V_CACHE).reshape(T, g.n_kv_heads, g.head_dim)
     pos = pos0 + sel
-    _, o64 = oracle.attention(q[sel], kc, vc, pos, g.n_q_heads, g.n_kv_heads, g.head_dim,
+    o, o64 = oracle.attention(q[sel], kc, vc, pos, g.n_q_heads, g.n_kv_heads, g.head_dim,
                               want64=True)
     # the same weights on |v|: the scale of each output's sum
     _, a64 = oracle.attention(q[sel], kc, abs_bits(vc), pos, g.n_q_heads, g.n_kv_heads,
                               g.head_dim, want64=True)
+    f = fp32_ref.attention(q[sel], kc, vc, pos, g.n_q_heads, g.n_kv_heads, g.head_dim)
     terms = np.repeat((pos + 1)[:, None], g.q_dim, axis=1)
     fast = kernel == "prompt-fast"
-    exact, ok = report(f"{kernel} attention, {rows} rows at {pos0}", out32.cpu().numpy()[sel],
-                       o64, u16(out)[sel], a64, terms, rel=2.0 ** -16 if fast else 0.0)
+    exact, ok = report(f"{kernel} attention, heads of {g.head_dim}, {rows} rows at {pos0} "
+                       f"(float32 reference: bf16 exact {float((f == o).mean()):.6f})",
+                       out32.cpu().numpy()[sel], o64, u16(out)[sel], a64, terms,
+                       rel=2.0 ** -16 if fast else 0.0)
     seq.close()
     assert ok and exact >= (0.995 if fast else 0.999)
+
+
+@pytest.mark.parametrize("kernel,rows,pos0", ATTN_CASES)
+def test_attention_kernels_vs_oracle(layer, kernel, rows, pos0):
+    _attention_case(layer, kernel, rows, pos0, 131072)
+
+
+SMALL_ATTN_CASES = [
+    *[(k, ROWS, 0) for k in ("prompt-exact", "prompt-fast")],
+    *[(k, 128, 129) for k in ("prompt-exact", "prompt-fast")],  # rows off the 64-slot key tiles
+    ("decode", 16, 4096),
+    ("decode", 16, 8176),  # a window ending at the last slot
+]
+
+
+@pytest.mark.parametrize("kernel,rows,pos0", SMALL_ATTN_CASES)
+def test_attention_kernels_heads_of_64(small_layer, kernel, rows, pos0):
+    _attention_case(small_layer, kernel, rows, pos0, 8192)

@@ -3,15 +3,19 @@
 1. Layer-local at the benchmark's shapes: executions of the 33B-shaped and
    the looped model (first, middle, last block) run as a whole prompt chunk
    of 2,048 / 512 rows -- the projection tiling and attention grid that the
-   benchmark times -- and as a one-row step at the workload's last decode
-   position, from synthetic states that reach the GPU and the oracle alike
-   (N(0,1) rows, caches of N(0,1) keys and values), >= 16 sampled rows spread
-   over the chunk down to the last compared per half; the long-context
-   workload's last prompt chunk over a 129,024-position cache likewise.  The
-   exact prompt form is held to 2 bf16 steps at max(|a|, |b|) on >= 99.9% of
-   elements; the fast form to 2 steps at the larger addend of the residual
-   add, its literal figure logged beside (its matrix-unit sums are measured
-   per kernel in tests/test_gpu_kernels.py).
+   benchmark times -- and as a 16-row decode window ending at the workload's
+   last decode position, from synthetic states that reach the GPU and the
+   oracle alike (N(0,1) rows, caches of N(0,1) keys and values), >= 16 sampled
+   rows spread over the chunk down to the last compared per half; the
+   long-context workload's last prompt chunk over a 129,024-position cache
+   likewise.  Each half is held to 2 bf16 steps at the larger addend of the
+   residual add on >= 99.9% of elements, and the halves of a test together
+   to 2 steps at max(|a|, |b|) on >= 99.9% or, where an ordinary float32
+   implementation of the same halves itself misses more than 0.05%, on 1 - 2x
+   its miss fraction (tests/gpu_util.HalfGates).  The prompt chunks' fast form
+   is held to the addend bar, its literal figures logged beside the float32
+   reference's (its matrix-unit sums are held per kernel in
+   tests/test_gpu_kernels.py); the exact form and decode to both.
 2. End to end: the oracle walks the first rows of the benchmark's prompt
    through every block (one block's weights at a time, as the float64
    reference in the pull request "llama: Nanbeige4.3-33B on Metal, the bf16
@@ -30,8 +34,8 @@ import pytest
 import oracle
 from oracle.model import OracleModel
 from synth.workloads import config
-from tests import parity
-from tests.gpu_util import HalfRunner, exec_inputs, half_report, log, to_dev, u16
+from tests import fp32_ref, parity
+from tests.gpu_util import KINDS, HalfGates, HalfRunner, exec_inputs, log, to_dev, u16
 from tests.host_inputs import HostWeights
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -112,24 +116,29 @@ def _run(cfg, sampled_execs):
     w = sd.weights(g)
     torch.cuda.synchronize()
 
-    # 1. sampled executions, layer-local per half, as prompt chunks
+    # 1. sampled executions, layer-local per half, as prompt chunks in both
+    # prompt forms, beside an ordinary float32 implementation of the same half
     runner = HalfRunner(g, w, 64, 64)
     runner_x = HalfRunner(g, w, 64, 64, prompt_exact=True)
     ins = exec_inputs(g, oracle.embed(W("embed"), ptoks[:SAMPLE_ROWS]), caps, W("final_norm"))
     empty = np.zeros((1, g.n_kv_heads, g.head_dim), dtype=np.uint16)
+    pos = np.arange(SAMPLE_ROWS, dtype=np.int32)
+    gates = {"fast": HalfGates(False), "exact": HalfGates(True)}
     for e in sampled_execs:
         b = e % g.n_blocks
         mid, outr = caps[e]
-        got_mid, _ = runner.run(b, ins[e], empty, empty, 0, "attn", chunk=True)
-        got_out, _ = runner.run(b, mid, empty, empty, 0, "mlp", chunk=True)
-        assert half_report(f"config {cfg} exec {e} attention half", got_mid, mid, ins[e],
-                           "addend") >= 0.999
-        assert half_report(f"config {cfg} exec {e} MLP half", got_out, outr, mid, "addend") >= 0.999
-        got_mid, _ = runner_x.run(b, ins[e], empty, empty, 0, "attn", chunk=True)
-        got_out, _ = runner_x.run(b, mid, empty, empty, 0, "mlp", chunk=True)
-        tag = f"config {cfg} exec {e} (exact prompt form)"
-        assert half_report(tag + " attention half", got_mid, mid, ins[e]) >= 0.999
-        assert half_report(tag + " MLP half", got_out, outr, mid) >= 0.999
+        blk = {k: W(f"b{b}.{k}") for k in KINDS}
+        kc0 = np.zeros((SAMPLE_ROWS, g.n_kv_heads, g.head_dim), dtype=np.uint16)
+        f_mid = fp32_ref.attn_half(g, blk, kc0, kc0, pos, ins[e], pos)
+        f_out = fp32_ref.mlp_half(g, blk, mid)
+        for r, form in ((runner, "fast"), (runner_x, "exact")):
+            got_mid, _ = r.run(b, ins[e], empty, empty, 0, "attn", chunk=True)
+            got_out, _ = r.run(b, mid, empty, empty, 0, "mlp", chunk=True)
+            tag = f"config {cfg} exec {e} ({form} prompt form)"
+            gates[form].check(tag + " attention half", got_mid, mid, ins[e], f_mid)
+            gates[form].check(tag + " MLP half", got_out, outr, mid, f_out)
+    for form, hg in gates.items():
+        hg.finish(f"config {cfg} sampled executions, {form} prompt form")
 
     # 2. the head, layer-local
     err, kl, counts = _head_layer_local(g, w, h_out, ref64, refb)
@@ -176,14 +185,17 @@ def _run(cfg, sampled_execs):
 
 
 CHUNK_SAMPLE = (0, 1, 127, 128, 255, 256, 511, 640, 777, 1023, 1024, 1300, 1535, 1791, 2046, 2047)
+WINDOW = 16
 
 
 def _layer_local_at_shape(cfg, blocks, P, last_pos, exact, pos0=0):
     """Executions of a workload at its benchmarked shapes from synthetic
     states: a prompt chunk of P rows at positions pos0.. (over pos0 planted
     positions of N(0,1) keys and values), >= 16 sampled rows spread over it
-    down to the last compared per half, and a one-row decode step at
-    last_pos over a planted cache."""
+    down to the last compared per half, and a 16-row decode window whose last
+    row sits at last_pos over a planted cache.  Each half is also computed by
+    an ordinary float32 implementation (tests/fp32_ref.py) to set the literal
+    bar (tests/gpu_util.HalfGates)."""
     import synth
     from oracle.model import block_rows, mlp_half
     from synth import device as sd
@@ -194,11 +206,10 @@ def _layer_local_at_shape(cfg, blocks, P, last_pos, exact, pos0=0):
     torch.cuda.synchronize()
     rows = np.array(sorted({r for r in CHUNK_SAMPLE if r < P} | {P - 1}))
     runner = HalfRunner(g, w, max(pos0 + P, last_pos + 1), P, prompt_exact=exact)
-    gate = "literal" if exact else "addend"
     form = "exact" if exact else "fast"
+    chunk_gate, window_gate = HalfGates(exact), HalfGates(True)
     for b in blocks:
-        blk = {k: W(f"b{b}.{k}") for k in ("attn_norm", "q", "k", "v", "o", "mlp_norm", "gate",
-                                            "up", "down")}
+        blk = {k: W(f"b{b}.{k}") for k in KINDS}
         seed = 3600 + 10 * cfg + b
         h = synth.normal_bf16(P * g.hidden, seed, TensorIds.INPUT_ROWS).reshape(P, g.hidden)
         T = pos0 + P
@@ -209,35 +220,46 @@ def _layer_local_at_shape(cfg, blocks, P, last_pos, exact, pos0=0):
                 pos0, g.n_kv_heads, g.head_dim)
             vc[:pos0] = synth.normal_bf16(pos0 * g.kv_dim, seed, TensorIds.V_CACHE).reshape(
                 pos0, g.n_kv_heads, g.head_dim)
-        mid, _ = block_rows(g, blk, kc, vc, np.arange(pos0, T, dtype=np.int32), h, rows)
+        pos = np.arange(pos0, T, dtype=np.int32)
+        f_mid = fp32_ref.attn_half(g, blk, kc, vc, pos, h, rows)
+        mid, _ = block_rows(g, blk, kc, vc, pos, h, rows)
         got_mid, (gk, gv) = runner.run(b, h, kc, vc, pos0, "attn", chunk=True)
         tag = (f"config {cfg} block {b}, {P}-row chunk at {pos0}, rows {rows[0]}..{rows[-1]}, "
                f"{form} form")
-        assert half_report(tag + " attention half", got_mid[rows], mid, h[rows], gate) >= 0.999
+        chunk_gate.check(tag + " attention half", got_mid[rows], mid, h[rows], f_mid)
         for c, ref in ((gk[pos0:T], kc[pos0:]), (gv[pos0:T], vc[pos0:])):
             assert parity.within_ulps(c, ref)[0] >= 0.999
         del kc, vc, gk, gv
         h2 = synth.normal_bf16(P * g.hidden, seed + 5, TensorIds.INPUT_ROWS).reshape(P, g.hidden)
         got_out, _ = runner.run(b, h2, None, None, 0, "mlp", chunk=True)
-        out = mlp_half(g, blk, np.ascontiguousarray(h2[rows]))
-        assert half_report(tag + " MLP half", got_out[rows], out, h2[rows], gate) >= 0.999
-        if exact:  # the decode step does not depend on the prompt form
+        x2 = np.ascontiguousarray(h2[rows])
+        out = mlp_half(g, blk, x2)
+        chunk_gate.check(tag + " MLP half", got_out[rows], out, x2, fp32_ref.mlp_half(g, blk, x2))
+        if exact:  # decode windows do not depend on the prompt form
             continue
-        # the last decode step's position, over a synthetic cache
-        T = last_pos
-        kcd = np.zeros((T + 1, g.n_kv_heads, g.head_dim), dtype=np.uint16)
+        # a decode window ending at the workload's last position, over a
+        # synthetic cache
+        T = last_pos + 1 - WINDOW
+        kcd = np.zeros((last_pos + 1, g.n_kv_heads, g.head_dim), dtype=np.uint16)
         vcd = np.zeros_like(kcd)
         kcd[:T] = synth.normal_bf16(T * g.kv_dim, seed, TensorIds.K_CACHE).reshape(
             T, g.n_kv_heads, g.head_dim)
         vcd[:T] = synth.normal_bf16(T * g.kv_dim, seed, TensorIds.V_CACHE).reshape(
             T, g.n_kv_heads, g.head_dim)
-        hd = synth.normal_bf16(g.hidden, seed + 7, TensorIds.INPUT_ROWS).reshape(1, g.hidden)
+        hd = synth.normal_bf16(WINDOW * g.hidden, seed + 7, TensorIds.INPUT_ROWS).reshape(
+            WINDOW, g.hidden)
+        dpos = np.arange(T, last_pos + 1, dtype=np.int32)
+        wrows = np.arange(WINDOW)
+        f_dmid = fp32_ref.attn_half(g, blk, kcd, vcd, dpos, hd, wrows)
         got_dmid, _ = runner.run(b, hd, kcd, vcd, T, "attn", chunk=False)
-        dmid, dout = block_rows(g, blk, kcd, vcd, np.array([T], dtype=np.int32), hd, [0])
+        dmid, dout = block_rows(g, blk, kcd, vcd, dpos, hd, wrows)
         got_dout, _ = runner.run(b, dmid, kcd, vcd, T, "mlp", chunk=False)
-        tag = f"config {cfg} block {b}, decode row at position {T}"
-        assert half_report(tag + " attention half", got_dmid, dmid, hd) >= 0.999
-        assert half_report(tag + " MLP half", got_dout, dout, dmid) >= 0.999
+        tag = f"config {cfg} block {b}, {WINDOW}-row decode window at {T}..{last_pos}"
+        window_gate.check(tag + " attention half", got_dmid, dmid, hd, f_dmid)
+        window_gate.check(tag + " MLP half", got_dout, dout, dmid, fp32_ref.mlp_half(g, blk, dmid))
+    chunk_gate.finish(f"config {cfg}, {P}-row chunks at {pos0}, {form} form, blocks {blocks}")
+    if not exact:
+        window_gate.finish(f"config {cfg}, 16-row decode windows ending at {last_pos}, blocks {blocks}")
 
 
 @pytest.mark.parametrize("exact", [True, False])

@@ -2,9 +2,12 @@
 against the CPU oracle: ragged chunks spanning several 128-row tiles, a second
 chunk continuing at pos0 > 0 (continuity across chunk boundaries, as the
 NInfer card's "Validation" section checks), and a 33B-shaped layer over a
-4096-slot cache.  Layer-local halves within 2 bf16 steps on >= 99.9% of
-elements: at max(|a|, |b|) for the exact prompt form, at the larger addend of
-the residual add for the fast form (whose literal figure is logged beside);
+4096-slot cache.  Layer-local halves held by tests/gpu_util.HalfGates: each
+half within 2 bf16 steps at the larger addend of the residual add on >= 99.9%
+of elements, and for the exact prompt form the halves of a test together
+within 2 steps at max(|a|, |b|) on >= 99.9% (or 1 - 2x the miss fraction of
+an ordinary float32 implementation of the same halves where that exceeds
+0.05%); the fast form's literal figures are logged;
 logits max-abs 0.05 on the fp32 sums, KL <= 1e-3, top-1 >= 99% with
 near-ties only."""
 import numpy as np
@@ -14,7 +17,8 @@ import oracle
 from oracle.model import OracleModel
 from synth.workloads import TensorIds, config
 from tests import parity
-from tests.gpu_util import HalfRunner, exec_inputs, gpu_model, half_report, log, to_dev, u16
+from tests.gpu_util import (HalfGates, HalfRunner, exec_inputs, f32_halves, gpu_model, log, to_dev,
+                            u16)
 from tests.host_inputs import HostWeights
 
 pytestmark = pytest.mark.gpu
@@ -80,20 +84,22 @@ def test_chunk_layer_local(tiny200, chunk, exact):
     g, W = tiny200["g"], tiny200["W"]
     st = tiny200["steps"][chunk]
     runner = HalfRunner(g, sd.weights(g), 256, 256, prompt_exact=exact)
-    gate = "literal" if exact else "addend"
+    hg = HalfGates(exact)
     ins = exec_inputs(g, oracle.embed(W("embed"), st["tokens"]), st["caps"], W("final_norm"))
     for e in range(g.n_exec):
         mid, outr = st["caps"][e]
         kc0, vc0 = tiny200["kc"][e], tiny200["vc"][e]
         got_mid, (kc, vc) = runner.run(e % g.n_blocks, ins[e], kc0, vc0, st["pos0"], "attn")
         got_out, _ = runner.run(e % g.n_blocks, mid, kc0, vc0, st["pos0"], "mlp")
+        f_mid, f_out = f32_halves(g, W, e % g.n_blocks, kc0, vc0, st["pos0"], ins[e], mid)
         tag = f"tiny chunk {chunk} exec {e}" + (" (exact prompt form)" if exact else "")
-        assert half_report(tag + " attention half", got_mid, mid, ins[e], gate) >= 0.999
-        assert half_report(tag + " MLP half", got_out, outr, mid, gate) >= 0.999
+        hg.check(tag + " attention half", got_mid, mid, ins[e], f_mid)
+        hg.check(tag + " MLP half", got_out, outr, mid, f_out)
         n = st["pos0"] + len(st["tokens"])
         for c, ref in ((kc, kc0), (vc, vc0)):
             frac, worst = parity.within_ulps(c[st["pos0"]:n], ref[st["pos0"]:n])
             assert frac >= 0.999, (tag, frac, worst)
+    hg.finish(f"tiny chunk {chunk}" + (" (exact prompt form)" if exact else ""))
 
 
 @pytest.mark.parametrize("exact", [True, False])
@@ -123,14 +129,16 @@ def test_layer33_chunk_vs_oracle(exact):
     runner = HalfRunner(g, sd.weights(g), T + R, R, prompt_exact=exact)
     got_mid, (kcg, vcg) = runner.run(0, rows, kc, vc, T, "attn")
     got_out, _ = runner.run(0, mid, kc, vc, T, "mlp")
-    gate = "literal" if exact else "addend"
+    f_mid, f_out = f32_halves(g, W, 0, kc, vc, T, rows, mid)
     tag = "layer33 chunk" + (" (exact prompt form)" if exact else "")
-    a = half_report(tag + " attention half", got_mid, mid, rows, gate)
-    b = half_report(tag + " MLP half", got_out, h, mid, gate)
+    hg = HalfGates(exact)
+    hg.check(tag + " attention half", got_mid, mid, rows, f_mid)
+    hg.check(tag + " MLP half", got_out, h, mid, f_out)
+    hg.finish(tag)
     fk, _ = parity.within_ulps(kcg[T:], kco[T:])
     fv, _ = parity.within_ulps(vcg[T:], vco[T:])
     log(f"layer33 chunk cache slots: k {fk:.5f} v {fv:.5f}")
-    assert a >= 0.999 and b >= 0.999 and fk >= 0.999 and fv >= 0.999
+    assert fk >= 0.999 and fv >= 0.999
 
 
 @pytest.mark.parametrize("cfg,n,bad,exact", [(1, 200, 150, False), (2, 300, 211, False),
@@ -213,20 +221,22 @@ def test_degenerate_chunk_layer_local(edge, chunk, exact):
     st = edge["steps"][chunk]
     n = len(st["tokens"])
     runner = HalfRunner(g, sd.weights(g), EDGE_CAP, 128, prompt_exact=exact)
-    gate = "literal" if exact else "addend"
+    hg = HalfGates(exact)
     ins = exec_inputs(g, oracle.embed(W("embed"), st["tokens"]), st["caps"], W("final_norm"))
     for e in range(g.n_exec):
         mid, outr = st["caps"][e]
         kc0, vc0 = edge["kc"][e], edge["vc"][e]
         got_mid, (kc, vc) = runner.run(e % g.n_blocks, ins[e], kc0, vc0, st["pos0"], "attn", chunk=True)
         got_out, _ = runner.run(e % g.n_blocks, mid, kc0, vc0, st["pos0"], "mlp", chunk=True)
+        f_mid, f_out = f32_halves(g, W, e % g.n_blocks, kc0, vc0, st["pos0"], ins[e], mid)
         tag = f"edge chunk of {n} at {st['pos0']} exec {e}" + (" (exact)" if exact else "")
-        assert half_report(tag + " attention half", got_mid, mid, ins[e], gate) >= 0.999
-        assert half_report(tag + " MLP half", got_out, outr, mid, gate) >= 0.999
+        hg.check(tag + " attention half", got_mid, mid, ins[e], f_mid)
+        hg.check(tag + " MLP half", got_out, outr, mid, f_out)
         end = st["pos0"] + n
         for c, ref in ((kc, kc0), (vc, vc0)):
             frac, worst = parity.within_ulps(c[st["pos0"]:end], ref[st["pos0"]:end])
             assert frac >= 0.999, (tag, frac, worst)
+    hg.finish(f"edge chunk of {n} at {st['pos0']}" + (" (exact)" if exact else ""))
 
 
 def test_degenerate_chunk_logits(edge):

@@ -11,11 +11,15 @@ its decode path (sixteen 16-row windows per prompt), against the oracle.
 
 On random-init weights the top two logits of a row are often within a
 rounding-scale distance of each other, so the oracle itself changes its
-greedy choice on ~1.5% of rows when one input row is moved by one bf16 step.
-The gate is therefore relative to that: the GPU must disagree with the oracle
-on no more rows than the oracle nudged in that way does, and have no more red
-rows (contenders further apart than one step, or a third contender within
-it).  The absolute figure (the pages' 99%) is printed beside it."""
+greedy choice on ~1.5% of rows when one input row is moved by one bf16 step,
+and an ordinary float32 implementation of the same spec (tests/fp32_ref.py)
+differs from the binary64 oracle on about as many.  The gate is therefore
+relative to those two in-spec references: with lam the larger of their miss
+counts, the GPU may miss on at most lam + 3 sqrt(lam) + 2 rows (the upper end
+of a Poisson count of that mean), and likewise for red rows (contenders
+further apart than one step, or a third contender within it).  The absolute
+figure (the pages' 99%) is printed beside it.
+"""
 import dataclasses
 
 import numpy as np
@@ -24,7 +28,7 @@ import pytest
 import oracle
 from oracle.model import OracleModel
 from synth.workloads import config
-from tests import parity
+from tests import fp32_ref, parity
 from tests.gpu_util import gpu_model, log, to_dev, u16
 from tests.host_inputs import HostWeights
 
@@ -91,9 +95,15 @@ def test_teacher_forced_agreement(name):
     model.check_finite()
     n = ref64.shape[0]
     ncounts, ndetail = parity.judge(parity.bf16_bits_to_f64(refb), parity.bf16_bits_to_f64(nudgedb))
-    nmiss = n - ncounts["equal"]
+    fb = np.concatenate([fp32_ref.forward(g, W, toks)[1] for toks in prompts])
+    fcounts, fdetail = parity.judge(parity.bf16_bits_to_f64(refb), parity.bf16_bits_to_f64(fb))
     log(f"{name}: the oracle nudged by one step on the first row of each prompt: {ncounts} "
-        f"({100 * ncounts['equal'] / n:.2f}% equal over {n} positions)")
+        f"({100 * ncounts['equal'] / n:.2f}% equal over {n} positions); the float32 "
+        f"implementation: {fcounts} ({100 * fcounts['equal'] / n:.2f}% equal)")
+    lam = max(n - ncounts["equal"], n - fcounts["equal"])
+    lam_red = max(ncounts["red"], fcounts["red"])
+    bound = lam + 3.0 * np.sqrt(lam) + 2
+    bound_red = lam_red + 3.0 * np.sqrt(lam_red) + 2
     for path, (l32, lb) in paths.items():
         l32, lb = np.concatenate(l32), np.concatenate(lb)
         counts, detail = parity.judge(parity.bf16_bits_to_f64(refb), parity.bf16_bits_to_f64(lb))
@@ -102,7 +112,8 @@ def test_teacher_forced_agreement(name):
         kl = parity.mean_kl(ref64, l32)
         log(f"{name} {path} path, {n} teacher-forced positions: {counts} "
             f"({100 * counts['equal'] / n:.2f}% equal; the pages' bar is 99%), logits max|d| "
-            f"{err:.3e}, KL {kl:.2e}; misses {detail[:12]}")
-        assert miss <= nmiss, (path, counts, ncounts)
-        assert counts["red"] <= ncounts["red"], (path, counts, ncounts)
+            f"{err:.3e}, KL {kl:.2e}; misses {detail[:12]}; bounds {bound:.1f} misses, "
+            f"{bound_red:.1f} red")
+        assert miss <= bound, (path, counts, ncounts, fcounts)
+        assert counts["red"] <= bound_red, (path, counts, ncounts, fcounts)
         assert kl <= 1e-3

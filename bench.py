@@ -12,6 +12,9 @@ roofline fraction, and the CPU oracle timed on a bounded sample.
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --copy-probe-mib N    # a plain device copy of N MiB, for
                                           # calibrating HBM byte counters
+    python bench.py --request-only        # one headline request (prompt chunk +
+                                          # decode steps) and nothing else, for
+                                          # counter runs under a profiler
 """
 import argparse
 import hashlib
@@ -378,6 +381,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--request-only", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU: the forward step has no multi-GPU path "
@@ -425,6 +429,12 @@ def main():
         e2.record(stream)
         return e0, e1, e2, buf
 
+    if args.request_only:
+        request()
+        torch.cuda.synchronize()
+        model.check_finite()
+        log("one request done")
+        return
     for i in range(args.warmup):
         log(f"warmup step {i}")
         request()

@@ -77,6 +77,9 @@ _SIGS = {
     "llama_check_finite": (ctypes.c_int, [_P, _P]),
     "llama_sample": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                     ctypes.c_int32, ctypes.c_float, _P, _P, _P]),
+    "llama_sample_noalloc": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            ctypes.c_float, ctypes.c_int32, ctypes.c_float, _P,
+                                            _P, _P]),
     "llama_draft_round": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P,
                                           ctypes.POINTER(ctypes.c_int32), _P]),
     "llama_draft_round_sampled": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P,
@@ -235,6 +238,12 @@ def llama_check_finite(model, stream=None):
 def llama_sample(model, logits_bf16, rows, ld, temperature, top_k, top_p, u, tokens, stream=None):
     return _check(lib.llama_sample(model, logits_bf16, rows, ld, temperature, top_k, top_p, u,
                                    tokens, stream))
+
+
+def llama_sample_noalloc(logits_bf16, vocab, rows, ld, temperature, top_k, top_p, u, tokens,
+                         stream=None):
+    return _check(lib.llama_sample_noalloc(logits_bf16, vocab, rows, ld, temperature, top_k, top_p,
+                                           u, tokens, stream))
 
 
 def llama_draft_round(target, target_kv, draft, draft_kv, n_draft, last_token, tokens_out,

@@ -19,6 +19,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int CHUNK = 4096;
@@ -160,6 +162,60 @@ __global__ __launch_bounds__(256) void sample_final_kernel(const float* __restri
 }  // namespace
 
 int sample_chunks(int V) { return (V + CHUNK - 1) / CHUNK; }
+
+// ---------------------------------------------------------------------------
+// Scratch of the variant that allocates nothing (llama_sample_noalloc): the
+// candidates, the per-chunk non-finite marks and a flag word live in this
+// fixed device array, one copy per GPU for the life of the process.  Host
+// code never uses the symbol itself (on the host it only names a stand-in):
+// each device's address comes from hipGetSymbolAddress, looked up once per
+// device with that device current.
+constexpr size_t SCRATCH_CAND = (size_t)SAMPLE_NOALLOC_MAX_ROWS * SAMPLE_NOALLOC_MAX_CAND;
+constexpr size_t SCRATCH_BYTES =
+    2 * SCRATCH_CAND * 4 + (size_t)SAMPLE_NOALLOC_MAX_ROWS * SAMPLE_NOALLOC_MAX_CHUNKS * 4 + 256;
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+size_t sample_noalloc_scratch_bytes() { return SCRATCH_BYTES; }
+
+// Device address of this device's scratch array, or nullptr (*err set) if the
+// lookup fails.  Cached per device; the lookup runs once per device.
+static uint8_t* scratch_ptr(hipError_t* err) {
+  static std::mutex mu;
+  static uint8_t* ptrs[64] = {};
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptrs[dev] = (uint8_t*)p;
+  }
+  return ptrs[dev];
+}
+
+hipError_t launch_sample_noalloc(const void* logits, int V, int64_t ld, int rows, int k,
+                                 float temperature, float top_p, const float* u, int32_t* out,
+                                 hipStream_t s) {
+  hipError_t err;
+  uint8_t* base = scratch_ptr(&err);
+  if (!base) return err;
+  float* cv = (float*)base;
+  int* ci = (int*)(base + SCRATCH_CAND * 4);
+  int* bad = (int*)(base + 2 * SCRATCH_CAND * 4);
+  int* flag = (int*)(base + SCRATCH_BYTES - 256);
+  // every candidate and mark is written before it is read; the flag word is
+  // only ever raised, so it is cleared on each call (a fill kernel, not a
+  // memset, so the call may sit in a captured graph)
+  launch_fill_zero(flag, 1, s);
+  launch_sample(logits, V, ld, rows, k, temperature, top_p, u, cv, ci, bad, out, flag, s);
+  return hipGetLastError();
+}
 
 void launch_sample(const void* logits, int V, int64_t ld, int rows, int k, float temperature,
                    float top_p, const float* u, float* cv, int* ci, int* bad, int32_t* out,

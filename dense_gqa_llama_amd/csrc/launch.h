@@ -35,6 +35,17 @@ int sample_chunks(int V);
 void launch_sample(const void* logits, int V, int64_t ld, int rows, int k, float temperature,
                    float top_p, const float* u, float* cv, int* ci, int* bad, int32_t* out,
                    int* flag, hipStream_t s);
+// The same draw with its candidates in a fixed per-device scratch array
+// instead of a workspace (no allocation, no workspace): rows <=
+// SAMPLE_NOALLOC_MAX_ROWS, sample_chunks(V) * k <= SAMPLE_NOALLOC_MAX_CAND,
+// sample_chunks(V) <= SAMPLE_NOALLOC_MAX_CHUNKS (checked by the caller).
+#define SAMPLE_NOALLOC_MAX_ROWS 64
+#define SAMPLE_NOALLOC_MAX_CAND 4096
+#define SAMPLE_NOALLOC_MAX_CHUNKS 256
+size_t sample_noalloc_scratch_bytes();
+hipError_t launch_sample_noalloc(const void* logits, int V, int64_t ld, int rows, int k,
+                                 float temperature, float top_p, const float* u, int32_t* out,
+                                 hipStream_t s);
 void launch_argmax(const void* logits, int V, int ld, int rows, float* pv, int* pi, int32_t* out,
                    int* flag, hipStream_t s);
 // Acceptance of a drafted round: win[0..k] window inputs, t[0..k] the

@@ -855,6 +855,35 @@ int llama_test_attention(llama_model* m, int32_t prompt_kernel, llama_kv* kv, in
   return dev_check("test attention launch");
 }
 
+int llama_sample_noalloc(const void* logits, int32_t vocab, int32_t rows, int64_t ld,
+                         float temperature, int32_t top_k, float top_p, const float* u,
+                         int32_t* tokens, void* hip_stream) {
+  static_assert(LLAMA_SAMPLE_MAX_ROWS <= SAMPLE_NOALLOC_MAX_ROWS, "scratch rows");
+  static_assert((size_t)(LLAMA_SAMPLE_NOALLOC_MAX_VOCAB + 4095) / 4096 <= SAMPLE_NOALLOC_MAX_CHUNKS,
+                "scratch chunks");
+  if (!logits || !u || !tokens) return fail(LLAMA_E_ARG, "NULL buffer");
+  if (vocab < 1 || vocab > LLAMA_SAMPLE_NOALLOC_MAX_VOCAB)
+    return fail(LLAMA_E_ARG, "vocab %d outside 1..%d", vocab, LLAMA_SAMPLE_NOALLOC_MAX_VOCAB);
+  if (rows < 1 || rows > LLAMA_SAMPLE_MAX_ROWS)
+    return fail(LLAMA_E_ARG, "rows %d outside 1..%d", rows, LLAMA_SAMPLE_MAX_ROWS);
+  if (ld < vocab) return fail(LLAMA_E_ARG, "row stride %lld below the vocabulary %d", (long long)ld, vocab);
+  if (!(temperature > 0.0f) || !(temperature < INFINITY))
+    return fail(LLAMA_E_ARG, "temperature must be positive and finite");
+  if (top_k < 1 || top_k > LLAMA_SAMPLE_MAX_TOP_K || top_k > vocab)
+    return fail(LLAMA_E_ARG, "top_k %d outside 1..%d", top_k, std::min(LLAMA_SAMPLE_MAX_TOP_K, vocab));
+  if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return fail(LLAMA_E_ARG, "top_p must lie in (0, 1]");
+  if ((int64_t)sample_chunks(vocab) * top_k > SAMPLE_NOALLOC_MAX_CAND)
+    return fail(LLAMA_E_ARG, "top_k %d too large for a vocabulary of %d (scratch holds %d candidates per row)",
+                top_k, vocab, SAMPLE_NOALLOC_MAX_CAND);
+  if (sample_noalloc_scratch_bytes() != LLAMA_SAMPLE_NOALLOC_SCRATCH_BYTES)
+    return fail(LLAMA_E_DEVICE, "scratch size mismatch");
+  (void)hipGetLastError();
+  const hipError_t e = launch_sample_noalloc(logits, vocab, ld, rows, top_k, temperature, top_p, u,
+                                             tokens, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(LLAMA_E_DEVICE, "sampling without allocation: %s", hipGetErrorString(e));
+  return LLAMA_OK;
+}
+
 int llama_check_finite(llama_model* m, void* hip_stream) {
   if (!m) return fail(LLAMA_E_ARG, "model is NULL");
   hipStream_t s = (hipStream_t)hip_stream;

@@ -291,6 +291,28 @@ int llama_sample(llama_model* model, const void* logits_bf16_dev, int32_t rows, 
                  float temperature, int32_t top_k, float top_p, const float* u_dev,
                  int32_t* tokens_dev, void* hip_stream);
 
+/* Seeded sampling that allocates nothing, for callers that cannot allocate
+ * device memory or keep a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): llama_sample's draw (same
+ * rule, same bits) on rows of bf16 logits with `vocab` entries, with no model
+ * handle.  Its candidates live in a fixed scratch array of about 2.1 MiB
+ * (LLAMA_SAMPLE_NOALLOC_SCRATCH_BYTES) that the library keeps on every GPU it
+ * runs on until the process ends; the first call on a device looks up that
+ * device's copy.  Limits: rows 1..LLAMA_SAMPLE_MAX_ROWS, vocab
+ * 1..LLAMA_SAMPLE_NOALLOC_MAX_VOCAB, top_k 1..LLAMA_SAMPLE_MAX_TOP_K (and at
+ * most vocab) with ceil(vocab / 4096) * top_k <= 4096; temperature, top_p, u
+ * and ld as llama_sample.  A row holding NaN or +-Inf yields -1 (there is no
+ * model flag to raise).  Every call on one GPU shares that GPU's scratch and
+ * it keeps the last call's contents: calls that overlap on one GPU (other
+ * streams or threads) race and must be serialised by the caller; calls on one
+ * stream are ordered.  Refusals return LLAMA_E_ARG before anything is
+ * enqueued; a failed scratch lookup returns LLAMA_E_DEVICE. */
+#define LLAMA_SAMPLE_NOALLOC_MAX_VOCAB 1048576
+#define LLAMA_SAMPLE_NOALLOC_SCRATCH_BYTES (2u * 64u * 4096u * 4u + 64u * 256u * 4u + 256u)
+int llama_sample_noalloc(const void* logits_bf16_dev, int32_t vocab, int32_t rows, int64_t ld,
+                         float temperature, int32_t top_k, float top_p, const float* u_dev,
+                         int32_t* tokens_dev, void* hip_stream);
+
 /* One round of drafted greedy decoding (issue "A llama family on Metal:
  * Nanbeige4.3-33B served from its bf16 release", follow-ups: a smaller Llama
  * on the same tokenizer drafting for the served model with replies

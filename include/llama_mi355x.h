@@ -96,7 +96,15 @@ typedef struct llama_model llama_model; /* opaque */
 typedef struct llama_kv llama_kv;       /* opaque: one sequence, every execution */
 
 /* Bytes of device workspace a model needs for caches of up to
- * `max_positions` positions; 0 if the configuration is refused. */
+ * `max_positions` positions; 0 if the configuration is refused (reason in
+ * llama_last_error).  Memory is sized up front from the positions the caller
+ * budgets, as the pull request "llama: Nanbeige4.3-33B on Metal, the bf16
+ * release served as published" sizes its caches from a context budget
+ * (section "How").  The workspace holds the residual, normed rows, q/k/v,
+ * attention output and SwiGLU rows of the largest pass (max(max_chunk_rows,
+ * max_seqs * max_window_rows) rows), decode attention partials, the per-pass
+ * RoPE table, logits scratch, argmax and sampling partials and the
+ * non-finite flag.  Host-only. */
 size_t llama_workspace_bytes(const llama_config* cfg, int32_t max_positions);
 
 /* Checks the geometry and records the weight and workspace addresses.
@@ -112,11 +120,22 @@ int llama_load_weights(const llama_config* cfg, const llama_block_weights* block
                        llama_model** out);
 
 /* Cache bytes for one sequence of up to max_positions positions:
- * executions * max_positions * n_kv_heads * head_dim * 2 (K, V) * 2 bytes. */
+ * executions * max_positions * n_kv_heads * head_dim * 2 (K, V) * 2 bytes --
+ * 16-bit keys and values, 208 KiB per position for the 33B shape (the card
+ * "Nanbeige4.3-33B EXL3", section "Which rung should I use?", prices the
+ * model's 16-bit cache at that).  Host-only; 0 for a NULL model or a
+ * non-positive count. */
 size_t llama_kv_bytes(const llama_model* model, int32_t max_positions);
 
-/* Wraps a caller-owned device buffer of llama_kv_bytes() bytes as an empty
- * cache (length 0).  max_positions may not exceed the model's. */
+/* Wraps a caller-owned device buffer of at least llama_kv_bytes() bytes as an
+ * empty cache (length 0) of one sequence: the cache a budget of
+ * max_positions positions buys (pull request section "How": caches sized from
+ * the context budget).  The buffer stays owned by the caller and must outlive
+ * the handle.  Refusals: LLAMA_E_ARG (NULL model, buffer or out),
+ * LLAMA_E_CAPACITY (max_positions outside 1..the model's max_positions),
+ * LLAMA_E_WORKSPACE (bytes below llama_kv_bytes).  Host-only: nothing is
+ * enqueued and the buffer is not touched (its contents are never read before
+ * they are written). */
 int llama_kv_alloc(llama_model* model, int32_t max_positions, void* device_buf, size_t bytes,
                    llama_kv** out);
 
@@ -357,7 +376,11 @@ int llama_draft_round_sampled(llama_model* target, llama_kv* target_kv, llama_mo
 
 /* Synchronises hip_stream, then reports LLAMA_E_NONFINITE if any greedy or
  * sampled draw since the last call met a non-finite logit row (and clears
- * the flag), else LLAMA_OK. */
+ * the flag), else LLAMA_OK.  A row holding NaN or +-Inf is refused rather than
+ * given a token, as the pull request's teacher-forced checker refuses such
+ * rows before it chooses or compares tokens (review reply "Non-finite
+ * rows"); the draw itself yields -1 for that row.  LLAMA_E_DEVICE if the
+ * flag cannot be read. */
 int llama_check_finite(llama_model* model, void* hip_stream);
 
 void llama_kv_free(llama_kv* kv);

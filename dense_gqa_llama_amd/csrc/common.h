@@ -66,10 +66,22 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 // input rows.  A full wave sums a row, lane l taking 16-byte vectors l,
 // l+64, ..., then the xor butterfly.  H is a multiple of 8.
 
-// binary64 -> bf16 bits, round to nearest even: truncate to fp32 and set the
-// last bit if anything was dropped (round to odd: 24 bits >= 8 + 2 make the
-// second rounding exact), then fp32 -> bf16.
+// binary64 -> bf16 bits, round to nearest even.  Inside bf16's normal range
+// (biased binary64 exponent 897..1150) the rounding is done on the bits: add
+// half an ulp of bit 45 (less one, plus the kept lsb: ties to even), keep
+// sign, exponent and the top 7 mantissa bits, rebias the exponent by
+// 1023 - 127 (a carry into the exponent rounds up correctly, to Inf past the
+// largest value).  Elsewhere (zero, bf16 subnormals, Inf, NaN) through fp32
+// with round to odd -- truncate and set the last bit if anything was dropped,
+// 24 bits >= 8 + 2 making the second rounding exact -- then fp32 -> bf16.
 __device__ __forceinline__ bf16_t d2bf(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t e = (uint32_t)(b >> 52) & 0x7FFu;
+  if (e >= 897u && e <= 1150u) {
+    b += 0x00000FFFFFFFFFFFull + ((b >> 45) & 1ull);
+    const uint32_t t = (uint32_t)(b >> 45);  // sign | exponent (11) | mantissa (7)
+    return (bf16_t)((((t >> 18) & 1u) << 15) | ((t & 0x3FFFFu) - (896u << 7)));
+  }
   float f = __double2float_rz(x);
   if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);
   return f2bf(f);

@@ -128,6 +128,13 @@ def test_projection_kernels_vs_oracle(layer, name):
     Wa = abs_bits(Wh)
     _, a64 = oracle.linear(abs_bits(x[SAMPLE]), Wa, want64=True)
     ex_p, ok_p = report(f"{name} {n}x{k} prompt GEMM (M={ROWS})", g32, y64, gb, a64, k)
+    # planted control: the oracle with its last term dropped must fail the gate
+    xd0 = x[SAMPLE].copy()
+    xd0[:, -1] = 0
+    _, bad64 = oracle.linear(xd0, Wh, want64=True)
+    ex_c, ok_c = report(f"{name} planted control (oracle without its last term)", g32, bad64, gb,
+                        a64, k)
+    assert not (ok_c and ex_c >= 0.999), "the comparator did not see a dropped term"
     # the exact prompt form: sums restarted every 128 terms
     B.llama_test_linear(m, 2, xd.data_ptr(), ROWS, Wd.data_ptr(), n, k, y.data_ptr(),
                         y32.data_ptr(), torch.cuda.current_stream().cuda_stream)
@@ -218,14 +225,25 @@ def _attention_case(layer, kernel, rows, pos0, max_positions):
     _, a64 = oracle.attention(q[sel], kc, abs_bits(vc), pos, g.n_q_heads, g.n_kv_heads,
                               g.head_dim, want64=True)
     f = fp32_ref.attention(q[sel], kc, vc, pos, g.n_q_heads, g.n_kv_heads, g.head_dim)
+    # planted control: the oracle attending one position short (off by one in
+    # the causal bound) must fail the gate; rows at position 0 have no such
+    # control
+    keep = pos > 0
+    _, bad64 = oracle.attention(q[sel][keep], kc, vc, pos[keep] - 1, g.n_q_heads, g.n_kv_heads,
+                                g.head_dim, want64=True)
     terms = np.repeat((pos + 1)[:, None], g.q_dim, axis=1)
     fast = kernel == "prompt-fast"
     exact, ok = report(f"{kernel} attention, heads of {g.head_dim}, {rows} rows at {pos0} "
                        f"(float32 reference: bf16 exact {float((f == o).mean()):.6f})",
                        out32.cpu().numpy()[sel], o64, u16(out)[sel], a64, terms,
                        rel=2.0 ** -16 if fast else 0.0)
+    bar = 0.995 if fast else 0.999
+    ex_c, ok_c = report(f"{kernel} planted control (oracle one position short)",
+                        out32.cpu().numpy()[sel][keep], bad64, u16(out)[sel][keep], a64[keep],
+                        terms[keep], rel=2.0 ** -16 if fast else 0.0)
+    assert not (ok_c and ex_c >= bar), "the comparator did not see a missing key"
     seq.close()
-    assert ok and exact >= (0.995 if fast else 0.999)
+    assert ok and exact >= bar
 
 
 @pytest.mark.parametrize("kernel,rows,pos0", ATTN_CASES)

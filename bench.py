@@ -731,6 +731,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
         result["cpu_baseline"] = cpu_baseline(g, int(avg_T))
+        log("cpu baseline at the long context (oracle sample)")
+        result["long_context"]["cpu_baseline"] = cpu_baseline(g, LONG_T + LONG_ROUNDS // 2, reps=2)
     print(json.dumps(result), flush=True)
 
 

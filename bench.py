@@ -458,7 +458,7 @@ def main():
         f"first tokens {toks[:8]}")
 
     # dominant kernel: the decode gate/up projection (53% of a token's bytes)
-    # event pairs around the decode launches only (the prompt chunk is excluded)
+    # each decode launch's own execution time (the prompt chunk is excluded)
     request(before_decode=lambda: B.llama_set_timing(model.handle, "gate_up", g.n_exec * D))
     torch.cuda.synchronize()
     ms, n = B.llama_timing_read(model.handle)
@@ -476,7 +476,7 @@ def main():
         t, k = B.llama_timing_read(model.handle)
         B.llama_set_timing(model.handle, "off")
         return t, k
-    gemm_ms, _ = timed_prefill("prefill_gemm", 4 * g.n_exec)
+    gemm_ms, _ = timed_prefill("prefill_gemm", 6 * g.n_exec)
     attn_ms, _ = timed_prefill("prefill_attn", g.n_exec)
     gemm_tf = prefill_gemm_flops(g, P) / (gemm_ms / 1e3) / 1e12
     attn_tf = prefill_attn_flops(g, P) / (attn_ms / 1e3) / 1e12
@@ -506,7 +506,7 @@ def main():
         return a.elapsed_time(b), t
     exact_chunk()  # warm
     xms = min(exact_chunk()[0] for _ in range(args.steps))
-    xg = exact_chunk("prefill_gemm", 4 * g.n_exec)[1]
+    xg = exact_chunk("prefill_gemm", 6 * g.n_exec)[1]
     xa = exact_chunk("prefill_attn", g.n_exec)[1]
     prefill_exact = {"tok_s": round(P / (xms / 1e3), 1), "ms_per_chunk": round(xms, 2),
                      "gemm_ms": round(xg, 2),
@@ -639,7 +639,7 @@ def main():
         model.decode(lseqs, tokens=ltok, want_logits=False, next_out=ltok)
     b.record(stream)
     torch.cuda.synchronize()
-    ams, an = B.llama_timing_read(model.handle)
+    ams, _ = B.llama_timing_read(model.handle)
     B.llama_set_timing(model.handle, "off")
     lms = a.elapsed_time(b) / LONG_ROUNDS
     T_avg = LONG_T + (LONG_ROUNDS - 1) / 2.0  # positions before each round's rows
@@ -648,9 +648,9 @@ def main():
     long_ctx = {"positions": LONG_T, "sequences": 2, "ms_per_round": round(lms, 3),
                 "tok_s": round(2 / (lms / 1e3), 2),
                 "hbm_gbs": round(lbytes / (lms / 1e3) / 1e9, 1),
-                "attention_us_per_block": round(ams * 1e3 / max(an, 1), 2),
+                "attention_us_per_block": round(ams * 1e3 / (g.n_exec * LONG_ROUNDS), 2),
                 "attention_gbs": round(2 * (T_avg + 2) * kvp / g.n_exec
-                                       / (ams / max(an, 1) / 1e3) / 1e9, 1),
+                                       / (ams / (g.n_exec * LONG_ROUNDS) / 1e3) / 1e9, 1),
                 "prompt_chunk": lchunk, "prompt_prefill": lprefill}
     log(f"long context: {long_ctx}")
     del lseqs

@@ -253,9 +253,9 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
 template <int D, int G>
 void launch_dg(const void* q, const RowTable& tab, int rows, int nq, int nkv, float* part,
                int nb_launch, void* out, float* out32, hipStream_t s) {
-  hipLaunchKernelGGL((attn_decode_kernel<D, G>), dim3(nb_launch, nkv, rows), dim3(256), 0, s,
+  launch_k((attn_decode_kernel<D, G>), dim3(nb_launch, nkv, rows), dim3(256), 0, s,
                      (const bf16_t*)q, tab, nq, nkv, part);
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(nq, rows), dim3(D), 0, s, part, tab, nq,
+  launch_k((attn_merge_kernel<D>), dim3(nq, rows), dim3(D), 0, s, part, tab, nq,
                      (bf16_t*)out, out32);
 }
 

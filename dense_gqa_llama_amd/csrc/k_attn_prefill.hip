@@ -384,7 +384,7 @@ static void launch_dx(const void* q, const void* kc, const void* vc, int rows, i
                       int nkv, void* out, float* out32, hipStream_t s) {
   const int G = nq / nkv;
   dim3 grid((rows + QT - 1) / QT * nkv * (G % 2 + 2 * (G / 2)));
-  hipLaunchKernelGGL((attn_prefill_kernel<D, EXACT>), grid, dim3(256), 0, s, (const bf16_t*)q,
+  launch_k((attn_prefill_kernel<D, EXACT>), grid, dim3(256), 0, s, (const bf16_t*)q,
                      (const bf16_t*)kc, (const bf16_t*)vc, rows, pos0, nq, nkv, (bf16_t*)out,
                      out32);
 }

@@ -539,7 +539,7 @@ void launch_alt_nt(const GemmArgs& a, int ncols, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  hipLaunchKernelGGL((gemm_alt_kernel<EPI, BN, NTW>), dim3(nt), dim3(512), lds, s, a, mtiles);
+  launch_k((gemm_alt_kernel<EPI, BN, NTW>), dim3(nt), dim3(512), lds, s, a, mtiles);
 }
 
 // Weight copies are non-temporal when the activation operand exceeds 64 MB:
@@ -563,7 +563,7 @@ void launch_tile(const GemmArgs& a, int ncols, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, BK, FLUSH>), dim3(nt),
+  launch_k((gemm_kernel<BM, BN, WM, WN, EPI, BK, FLUSH>), dim3(nt),
                      dim3((BM / WM) * (BN / WN) * 64), lds, s, a, mtiles);
 }
 

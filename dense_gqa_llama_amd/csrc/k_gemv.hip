@@ -382,9 +382,9 @@ static void launch_r(GemvArgs a, int N, hipStream_t s) {
   // one-wave workgroups instead, every wave doing the same arithmetic (measured
   // on that model: down 17.3 -> 15.2 us, decode 308 -> 317 tok/s).
   if (R == 1 && grid < 256)
-    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, P, 1>), dim3(grid * 4), dim3(64), xbytes, s, a);
+    launch_k((gemv_kernel<R, NR, EPI, NORM, P, 1>), dim3(grid * 4), dim3(64), xbytes, s, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<R, NR, EPI, NORM, P, 4>), dim3(grid), dim3(256), xbytes, s, a);
+    launch_k((gemv_kernel<R, NR, EPI, NORM, P, 4>), dim3(grid), dim3(256), xbytes, s, a);
 }
 
 // Inputs are normalised inside the projection for windows of up to

@@ -1,8 +1,32 @@
 // Host-side launchers of the gfx950 kernels (defined in the k_*.hip files and
 // called by the C-ABI layer in llama_abi.cpp).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+// Kernel timing for benchmarks: while a timer is set on the calling thread,
+// each kernel launched through launch_k records the start and the end of its
+// own execution in the timer's next event pair (hipExtLaunchKernel), so the
+// pair spans the kernel alone, not the dispatch around it; once the pool is
+// used up, launches are not recorded.
+struct LaunchTimer {
+  hipEvent_t* ev;
+  size_t cap;
+  size_t* used;
+};
+extern __thread LaunchTimer* launch_timer __attribute__((visibility("hidden")));
+template <typename F, typename... A>
+inline void launch_k(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, A... args) {
+  LaunchTimer* t = launch_timer;
+  if (t && *t->used + 2 <= t->cap) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t->ev[*t->used], t->ev[*t->used + 1], 0,
+                          args...);
+    *t->used += 2;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
+}
 
 #define LLAMA_MAX_SEQS 16
 

@@ -14,6 +14,8 @@
 
 #include "launch.h"
 
+__attribute__((visibility("hidden"))) __thread LaunchTimer* launch_timer = nullptr;
+
 namespace {
 
 thread_local std::string g_err;
@@ -191,20 +193,21 @@ RowTable table_for(const Pass& p, int exec) {
   return t;
 }
 
-// Event pair around launches of the measured kernel class.
+// While in scope for the measured kernel class, the kernels launched record
+// their own execution time in the model's event pool.
 struct Timed {
-  llama_model* m;
-  hipStream_t s;
+  LaunchTimer lt;
+  LaunchTimer* prev;
   bool on;
-  Timed(llama_model* m_, int cls, hipStream_t s_) : m(m_), s(s_) {
-    on = m->timing_kernel == cls && m->tused + 2 <= m->tev.size();
-    if (on) (void)hipEventRecord(m->tev[m->tused], s);
+  Timed(llama_model* m, int cls, hipStream_t) : prev(launch_timer) {
+    on = m->timing_kernel == cls;
+    if (on) {
+      lt = LaunchTimer{m->tev.data(), m->tev.size(), &m->tused};
+      launch_timer = &lt;
+    }
   }
   ~Timed() {
-    if (on) {
-      (void)hipEventRecord(m->tev[m->tused + 1], s);
-      m->tused += 2;
-    }
+    if (on) launch_timer = prev;
   }
 };
 

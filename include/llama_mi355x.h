@@ -264,12 +264,16 @@ int llama_test_attention(llama_model* model, int32_t prompt_kernel, llama_kv* kv
                          float* out32_dev, void* hip_stream);
 
 /* Measurement hook for benchmarks.  While `kernel` is one of the classes
- * below, every step records a HIP event pair on its own stream around each
- * launch of that class, from a pool of max_launches pairs created by this
- * call (host-side event objects; no device memory).  Launches beyond the pool
- * are not recorded.  kernel = LLAMA_TIMING_OFF releases the pool.
- * llama_timing_read synchronises on the recorded events and returns the
- * summed milliseconds and the number of launches since the previous read. */
+ * below, every kernel of that class that a step launches records the start
+ * and the end of its own execution in a HIP event pair (hipExtLaunchKernel,
+ * on the step's stream), from a pool of max_launches pairs created by this
+ * call (host-side event objects; no device memory).  A class may launch more
+ * than one kernel per block (decode attention: the split pass and the merge;
+ * prompt q/k/v: up to two launches; prompt gate/up and down are one class).
+ * Launches beyond the pool are not recorded.  kernel = LLAMA_TIMING_OFF
+ * releases the pool.  llama_timing_read synchronises on the recorded events
+ * and returns the summed milliseconds of the recorded kernels and their
+ * number since the previous read. */
 enum {
   LLAMA_TIMING_OFF = 0,
   LLAMA_TIMING_GATE_UP = 1,   /* decode gate/up projection with SwiGLU */

@@ -33,6 +33,22 @@ def test_every_declared_symbol_is_exported(root):
     assert sorted(B.EXPORTS) == names
 
 
+def test_no_undefined_thread_local_init_reference():
+    """A hidden thread-local declared in one file and defined in another makes
+    the compiler test a weak, hidden init function (_ZTH...) by its address;
+    left undefined in a shared library, that address reads as the load base,
+    not zero, and the first use calls into the ELF header.  The library's
+    thread-locals that cross files are __thread, which has no such function."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not found")
+    out = subprocess.run([nm, B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    bad = [l for l in out.splitlines() if " U _ZTH" in l or " w _ZTH" in l]
+    assert not bad, bad
+
+
 def cfg_of(g, **kw):
     base = dict(n_blocks=g.n_blocks, n_loops=g.n_loops, hidden=g.hidden, n_q_heads=g.n_q_heads,
                 n_kv_heads=g.n_kv_heads, head_dim=g.head_dim, ffn=g.ffn, vocab=g.vocab,

@@ -77,7 +77,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
   }
   // K fragments (A operand): lane l holds slot l%16 of the tile, dims
   // 8(l/16) + 32i; values: lane l holds pair l%DP of slots l/DP + NSG*j.
-  // Slots past the wave's range re-read its last slot (never used).
+  // Slots past the wave's range re-read its last slot (never used).  The
+  // loads are non-temporal: a step reads each layer's cache once, and 52
+  // layers' caches and weights pass through the caches between two reads of
+  // the same slot (in the 33B model: 2k context 0.7% more tok/s, 131k 3.9%).
   const bf16_t* kbase = tab.k[seq] + (size_t)g * D + dq;
   const uint32_t* vbase = (const uint32_t*)(tab.v[seq] + (size_t)g * D) + lane % DP;
   const int vg = lane / DP;
@@ -87,11 +90,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
     const int s0 = ws + t * TS;
     const int sk = min(s0 + hl, we - 1);
 #pragma unroll
-    for (int i = 0; i < KST; ++i) kq[set][i] = *(const bf16x8_t*)(kbase + (size_t)sk * kvd + 32 * i);
+    for (int i = 0; i < KST; ++i)
+      kq[set][i] = __builtin_nontemporal_load((const bf16x8_t*)(kbase + (size_t)sk * kvd + 32 * i));
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
       const int sv = min(s0 + vg + NSG * j, we - 1);
-      vq[set][j] = vbase[(size_t)sv * (kvd / 2)];
+      vq[set][j] = __builtin_nontemporal_load(vbase + (size_t)sv * (kvd / 2));
     }
   };
 

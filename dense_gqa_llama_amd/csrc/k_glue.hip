@@ -95,7 +95,8 @@ void launch_rope_table(const RowTable& tab, int rows, int d, float theta, void* 
 
 // Prompt chunks: RoPE on the q and k heads of each row of the projection
 // output qkv [rows][qd + 2*kvd], then k and v stored at slot p of the row's
-// cache.  One workgroup per row.
+// cache.  One workgroup per row; a thread takes eight neighbouring pairs of
+// one head (16-byte loads and stores of both halves).
 __global__ __launch_bounds__(256) void rope_kv_kernel(const bf16_t* __restrict__ qkv,
                                                       bf16_t* __restrict__ qout, RowTable tab,
                                                       int nq, int nkv, int d,
@@ -103,27 +104,40 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const bf16_t* __restrict__
   const int rt = blockIdx.x;
   const int seq = rt / tab.rows_per_seq;
   const int p = tab.pos0[seq] + rt % tab.rows_per_seq;
-  const int half = d / 2;
+  const int half = d / 2, ng = half / 8;  // eight-pair groups per head
   const int qd = nq * d, kvd = nkv * d;
   const bf16_t* src = qkv + (size_t)rt * (qd + 2 * kvd);
   bf16_t* kdst = tab.k[seq] + (size_t)p * kvd;
   bf16_t* vdst = tab.v[seq] + (size_t)p * kvd;
   const float2* cs = table + (size_t)rt * half;
-  const int items = (nq + nkv) * half;
+  const int items = (nq + nkv) * ng;
   for (int it = threadIdx.x; it < items; it += blockDim.x) {
-    const int hh = it / half, i = it % half;
+    const int hh = it / ng, i0 = 8 * (it % ng);
     const bf16_t* x = src + hh * d;  // q heads then k heads, contiguous
-    const float x1 = bf2f(x[i]), x2 = bf2f(x[i + half]);
-    const float2 c = cs[i];
-    const bf16_t o1 = f2bf(rbf(x1 * c.x) + rbf(-x2 * c.y));
-    const bf16_t o2 = f2bf(rbf(x2 * c.x) + rbf(x1 * c.y));
+    const u32x4_t a = *(const u32x4_t*)(x + i0), b = *(const u32x4_t*)(x + i0 + half);
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+    uint32_t o1w[4], o2w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t r1 = 0, r2 = 0;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float x1 = __uint_as_float(k ? aw[e] & 0xFFFF0000u : aw[e] << 16);
+        const float x2 = __uint_as_float(k ? bw[e] & 0xFFFF0000u : bw[e] << 16);
+        const float2 c = cs[i0 + 2 * e + k];
+        r1 |= (uint32_t)f2bf(rbf(x1 * c.x) + rbf(-x2 * c.y)) << (16 * k);
+        r2 |= (uint32_t)f2bf(rbf(x2 * c.x) + rbf(x1 * c.y)) << (16 * k);
+      }
+      o1w[e] = r1;
+      o2w[e] = r2;
+    }
     bf16_t* dst = hh < nq ? qout + (size_t)rt * qd + hh * d : kdst + (hh - nq) * d;
-    dst[i] = o1;
-    dst[i + half] = o2;
+    *(u32x4_t*)(dst + i0) = u32x4_t{o1w[0], o1w[1], o1w[2], o1w[3]};
+    *(u32x4_t*)(dst + i0 + half) = u32x4_t{o2w[0], o2w[1], o2w[2], o2w[3]};
   }
-  const uint32_t* vs = (const uint32_t*)(src + qd + kvd);
-  uint32_t* vd = (uint32_t*)vdst;
-  for (int i = threadIdx.x; i < kvd / 2; i += blockDim.x) vd[i] = vs[i];
+  const u32x4_t* vs = (const u32x4_t*)(src + qd + kvd);
+  u32x4_t* vd = (u32x4_t*)vdst;
+  for (int i = threadIdx.x; i < kvd / 8; i += blockDim.x) vd[i] = vs[i];
 }
 
 void launch_rope_kv(const void* qkv, void* qout, const RowTable& tab, int rows, int nq, int nkv,

@@ -9,7 +9,10 @@
 // each kernel launched through launch_k records the start and the end of its
 // own execution in the timer's next event pair (hipExtLaunchKernel), so the
 // pair spans the kernel alone, not the dispatch around it; once the pool is
-// used up, launches are not recorded.
+// used up, launches are not recorded.  The timer pointer is `__thread`, not
+// `thread_local`: a hidden thread_local used across files makes the compiler
+// test a thread-local init function by its address, and in a shared object an
+// undefined one reads as the load base rather than zero.
 struct LaunchTimer {
   hipEvent_t* ev;
   size_t cap;

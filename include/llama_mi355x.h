@@ -273,7 +273,8 @@ int llama_test_attention(llama_model* model, int32_t prompt_kernel, llama_kv* kv
  * Launches beyond the pool are not recorded.  kernel = LLAMA_TIMING_OFF
  * releases the pool.  llama_timing_read synchronises on the recorded events
  * and returns the summed milliseconds of the recorded kernels and their
- * number since the previous read. */
+ * number since the previous read.  While the hook is on, one host thread
+ * drives the model (the pool's cursor is not shared safely between threads). */
 enum {
   LLAMA_TIMING_OFF = 0,
   LLAMA_TIMING_GATE_UP = 1,   /* decode gate/up projection with SwiGLU */

@@ -15,6 +15,9 @@ roofline fraction, and the CPU oracle timed on a bounded sample.
     python bench.py --request-only        # one headline request (prompt chunk +
                                           # decode steps) and nothing else, for
                                           # counter runs under a profiler
+    python bench.py --vendor-gemm         # the 33B projections at 2,048 rows:
+                                          # this library's prompt GEMM beside the
+                                          # vendor library's (torch bf16 linear)
 """
 import argparse
 import hashlib
@@ -374,6 +377,63 @@ def bench_looped(stream, cpu):
     return out
 
 
+def vendor_gemm(reps=20):
+    """The four projections of one 33B block at 2,048 rows, each as one
+    STORE launch of this library's prompt GEMM (llama_test_linear; q/k/v as
+    one 9,216-column matrix, gate/up as one 44,032-column matrix) and as
+    torch's bf16 linear (the vendor BLAS), on the same operands, alternating,
+    best of two rounds of `reps` launches each.  Prints one JSON line."""
+    import torch
+    import dense_gqa_llama_amd as L
+    from dense_gqa_llama_amd import binding as B
+    from synth import device as sd
+    from synth.workloads import config
+    g = config(2)
+    w = sd.weights(g)
+    m = L.Model(g, w, max_positions=64, max_chunk_rows=2048, max_seqs=1)
+    st = torch.cuda.current_stream()
+    M = 2048
+    mats = {"qkv": torch.cat([w["b0.q"], w["b0.k"], w["b0.v"]]).contiguous(), "o": w["b0.o"],
+            "gate_up": torch.cat([w["b0.gate"], w["b0.up"]]).contiguous(), "down": w["b0.down"]}
+
+    def timed(call):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            call()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    rows, tot = {}, {"this": 0.0, "vendor": 0.0, "gflop": 0.0}
+    for name, Wd in mats.items():
+        n, k = Wd.shape
+        x = sd.normal((M, k), 3200, 0).view(torch.bfloat16)
+        y = torch.empty((M, n), dtype=torch.int16, device="cuda")
+        y32 = torch.empty((M, n), dtype=torch.float32, device="cuda")
+        ours = lambda: B.llama_test_linear(m.handle, 1, x.data_ptr(), M, Wd.data_ptr(), n, k,
+                                           y.data_ptr(), y32.data_ptr(), st.cuda_stream)
+        Wb = Wd.view(torch.bfloat16)
+        vendor = lambda: torch.nn.functional.linear(x, Wb)
+        ours(); vendor(); torch.cuda.synchronize()
+        t = {"this": 9e9, "vendor": 9e9}
+        for _ in range(2):
+            t["this"] = min(t["this"], timed(ours))
+            t["vendor"] = min(t["vendor"], timed(vendor))
+        gf = 2.0 * M * n * k / 1e9
+        rows[name] = {"n": n, "k": k, "gflop": round(gf, 1),
+                      "this_us": round(t["this"] * 1e3, 1), "vendor_us": round(t["vendor"] * 1e3, 1),
+                      "this_tflops": round(gf / t["this"], 1), "vendor_tflops": round(gf / t["vendor"], 1)}
+        tot["this"] += t["this"]
+        tot["vendor"] += t["vendor"]
+        tot["gflop"] += gf
+        log(f"{name}: {rows[name]}")
+    print(json.dumps({"workload": "33B projections at 2,048 rows, one STORE launch each",
+                      "rows": rows, "this_tflops": round(tot["gflop"] / tot["this"], 1),
+                      "vendor_tflops": round(tot["gflop"] / tot["vendor"], 1),
+                      "vendor": "torch.nn.functional.linear, bf16 (hipBLASLt)"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,6 +442,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0)
     ap.add_argument("--request-only", action="store_true")
+    ap.add_argument("--vendor-gemm", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU: the forward step has no multi-GPU path "
@@ -392,6 +453,9 @@ def main():
     import torch
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.vendor_gemm:
+        vendor_gemm()
         return
 
     import dense_gqa_llama_amd as L

@@ -1,7 +1,8 @@
 """GPU parity of the forward step through the C ABI, against the CPU oracle,
 on the same seeded inputs (inputs flow oracle -> GPU only).
 
-Gates (spec tolerances, with the readings stated in the design doc):
+Gates (the tolerances of the forward-step spec; where the pages leave a step open, the readings
+named beside each gate):
 - logits: the GPU's fp32 sums within 0.05 of the oracle's binary64 sums,
   mean KL at most 1e-3, teacher-forced top-1 agreement at least 99% with every
   difference a near-tie by the rule of the pull request "llama:

@@ -26,7 +26,8 @@
    executions, and the head fed the oracle's final residual through an
    identity block), and end to end the GPU's greedy choices may differ from
    the oracle's on no more rows than the oracle's own do under that one-step
-   change (and on at most one row when the nudged oracle has none).
+   change (and on at most one row when the nudged oracle has none), and its
+   logits' mean KL from the oracle's may not exceed the nudged oracle's.
 """
 import numpy as np
 import pytest
@@ -182,6 +183,9 @@ def _run(cfg, sampled_execs):
         f"the oracle nudged by one step: max|d| {np.abs(n64 - all64).max():.3e} KL "
         f"{parity.mean_kl(all64, n64):.2e}, judge {ncounts} {ndetail}")
     assert miss <= max(1, nmiss)
+    # the GPU's logits stay at least as close to the oracle's as the oracle's
+    # own do under the one-step change (mean KL over the compared rows)
+    assert kl <= parity.mean_kl(all64, n64), (kl, parity.mean_kl(all64, n64))
 
 
 CHUNK_SAMPLE = (0, 1, 127, 128, 255, 256, 511, 640, 777, 1023, 1024, 1300, 1535, 1791, 2046, 2047)

@@ -50,6 +50,16 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// The low bf16 half of w as an fp32 value (w << 16).  Written as one
+// instruction: from the plain shift the compiler rebuilds the half by
+// converting the weight alone again and shifting, one more instruction per
+// pair (2-3% of the fast form's time at 2k context).
+__device__ __forceinline__ float lo_half(uint32_t w) {
+  uint32_t r;
+  asm("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w));
+  return __uint_as_float(r);
+}
+
 // nonzero when either bf16 half of w has an all-ones exponent (Inf or NaN)
 __device__ __forceinline__ uint32_t nonfinite2(uint32_t w) {
   return ((w & 0x7F807F80u) + 0x00800080u) & 0x80008000u;
@@ -279,11 +289,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
             psum += p0;
             psum += p1;
             const uint32_t hw = cvt_pk_bf16(p0, p1);
-            const float r0 = p0 - __uint_as_float(hw << 16), r1 = p1 - __uint_as_float(hw & 0xFFFF0000u);
+            const float r0 = p0 - lo_half(hw), r1 = p1 - __uint_as_float(hw & 0xFFFF0000u);
             const uint32_t mw = cvt_pk_bf16(r0, r1);
             pk[i] = hw;
             pm[i] = mw;
-            pl[i] = cvt_pk_bf16(r0 - __uint_as_float(mw << 16), r1 - __uint_as_float(mw & 0xFFFF0000u));
+            pl[i] = cvt_pk_bf16(r0 - lo_half(mw), r1 - __uint_as_float(mw & 0xFFFF0000u));
           }
           pf[st] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
           pfm[st] = __builtin_bit_cast(bf16x8_t, u32x4_t{pm[0], pm[1], pm[2], pm[3]});
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
           psum += p1;
           const uint32_t hw = cvt_pk_bf16(p0, p1);
           pk[i] = hw;
-          pl[i] = cvt_pk_bf16(p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u));
+          pl[i] = cvt_pk_bf16(p0 - lo_half(hw), p1 - __uint_as_float(hw & 0xFFFF0000u));
         }
         const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
         const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, u32x4_t{pl[0], pl[1], pl[2], pl[3]});

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const bf16_t* __restri
   const int nb = p / kb + 1;
   if (b >= nb) return;  // uniform per workgroup
   const int start = b * kb, end = min(start + kb, p + 1);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ql = kb / 4;  // a multiple of 16
   const int ws = start + wave * ql, we = min(ws + ql, end);  // this wave's slots
   const int ntile = we > ws ? (we - ws + TS - 1) / TS : 0;

@@ -84,7 +84,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const bf16_t* __re
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][KT * D];
   __shared__ uint32_t sBad[2][4];  // per tile: slots whose value was not finite, 16 per wave
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index as a scalar: every LDS-direct copy's destination (M0) and
+  // the work unit's head and rows are then scalar arithmetic, not a lane
+  // read-back per copy (3-8% less time, same bits)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Work units per KV head g, 128 chunk rows (a span) at a time: the heads of
   // the group in pairs, each pair a workgroup of 64 rows (two waves per head),
   // so every staged key/value tile serves two heads; an odd last head takes

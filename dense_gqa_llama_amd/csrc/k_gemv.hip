@@ -86,7 +86,9 @@ __global__ __launch_bounds__(64 * WPB) void gemv_kernel(GemvArgs a) {
   extern __shared__ u32x4_t sx[];  // a chunk of the (normalised) input rows, [R][xcv]
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
   static_assert(EPI != GEMV_QKV_ROPE || NR == 4, "rotation pairs come four rows per wave");
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index as a scalar: row pointers and chunk bounds in scalar
+  // registers (the looped model's gate/up 22.6 -> 21.4 us, same bits)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * WPB + wave) * COLS;  // first output column of this wave
 
   const u32x4_t* wp[NR];

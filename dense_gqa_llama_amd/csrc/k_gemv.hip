@@ -87,8 +87,12 @@ __global__ __launch_bounds__(64 * WPB) void gemv_kernel(GemvArgs a) {
   constexpr int COLS = EPI == GEMV_SWIGLU ? NR / 2 : NR;
   static_assert(EPI != GEMV_QKV_ROPE || NR == 4, "rotation pairs come four rows per wave");
   // the wave index as a scalar: row pointers and chunk bounds in scalar
-  // registers (the looped model's gate/up 22.6 -> 21.4 us, same bits)
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // registers (the looped model's gate/up 22.6 -> 21.4 us, same bits).  For
+  // windows of 15-16 rows it stays a vector value: the kernel then holds
+  // enough registers for three waves per SIMD instead of four, which those
+  // windows run faster (16 rows: 407 against 419 us per 33B layer).
+  const int wave = R >= 15 ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * WPB + wave) * COLS;  // first output column of this wave
 
   const u32x4_t* wp[NR];
